@@ -1,0 +1,81 @@
+"""The pins are strong enough: each plausible slip in the oracle fails one.
+
+Every mutant below is the oracle source with one deliberate mistake, compiled
+to a temporary library on the CPU.  The pin suite of test_oracle_pins must
+reject every one of them (and accept the unmodified source).
+"""
+
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "interleaved_gqa_groups": ("int g = h / (p->Hq / p->Hkv);", "int g = h % p->Hkv;"),
+    "dropped_softmax_scale": ("s[t - t0] = p->scale * dot;", "s[t - t0] = dot;"),
+    "no_max_subtraction": ("double w = exp(s[t - t0] - M);", "double w = exp(s[t - t0]);"),
+    "unnormalised_output": ("o[d] = acc[d] / Z;", "o[d] = acc[d];"),
+    "int8_scale_ignored": ("x = (double)sc[tile] * x;", "x = 1.0 * x;"),
+    "values_read_from_keys": ("const void *base = which ? p->v_pages : p->k_pages;",
+                              "const void *base = p->k_pages;"),
+    "pool_layout_head_major": ("size_t tile = ((size_t)row * p->Hkv + g) * p->PS + slot;",
+                               "size_t tile = ((size_t)g * p->n_host_pages + row) * p->PS + slot;"),
+    "key_slot_off_by_one": ("kv_elem(p, 0, row, g, t % p->PS, d)",
+                            "kv_elem(p, 0, row, g, (t + 1) % p->PS, d)"),
+    "query_transposed": ("size_t qoff = ((size_t)b * p->Hq + h) * p->D;",
+                         "size_t qoff = ((size_t)h * p->B + b) * p->D;"),
+    "f16_subnormal_exponent": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "f16_sign_lost": ("return sign ? -v : v;", "return v;"),
+    "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "split_merge_missing_rescale": ("L += l[k] * exp(m[k] - M);", "L += l[k];"),
+    "split_partition_max_wrong": ("m[k] = mk;", "m[k] = 0.0;"),
+}
+
+PIN_SUITE = [
+    lambda: pins.test_f16_decode_matches_numpy_all_patterns(oracle.lib()),
+    lambda: pins.test_bf16_decode_matches_torch_all_patterns(oracle.lib()),
+    *[(lambda s=s: pins.test_oracle_matches_pure_python_brute_force(s)) for s in pins.TINY_SHAPES],
+    *[(lambda T=T: pins.test_split_merge_matches_unsplit(T)) for T in (16, 64)],
+    pins.test_large_common_score_shift_is_harmless,
+    pins.test_gqa_equals_mha_with_repeated_kv_heads_bitwise,
+    pins.test_int8_with_unit_scales_equals_f16_of_same_integers,
+]
+
+
+def run_suite_against(src_text):
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "mutant.c")
+        with open(src, "w") as f:
+            f.write(src_text)
+        so = oracle.build(src=src, out=os.path.join(d, "libmutant.so"))
+        prev = oracle.set_lib(oracle.load(so))
+        failures = 0
+        try:
+            for check in PIN_SUITE:
+                try:
+                    check()
+                except (AssertionError, oracle.OracleError, ValueError):
+                    failures += 1
+        finally:
+            oracle.set_lib(prev)
+        return failures
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC_PATH) as f:
+        return f.read()
+
+
+def test_unmodified_source_passes_the_suite(source):
+    assert run_suite_against(source) == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(source, name):
+    old, new = MUTANTS[name]
+    assert old in source, f"mutation site of {name} not found"
+    assert run_suite_against(source.replace(old, new)) > 0
