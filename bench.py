@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of paged single-token decode attention on one MI355X.
+
+One step = one decode call over every sequence of one layer (the partition
+kernel, then the split-K reduce kernel when sequences span several
+partitions), on synthetic inputs already resident in HBM.  Layers are rotated
+(distinct pool buffers with the same contents) so the 256 MB Infinity Cache
+cannot serve a layer from the previous step.
+
+Prints ONE JSON line: value = algorithmic HBM bytes per step / time per step
+(GB/s), with the per-kernel roofline of the partition kernel (timed with HIP
+events on the stream it runs on) and the fp64 oracle timed on this host's
+cores as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+DEFAULT_CONFIG = "llama3_8b_gqa"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="distinct layer buffers cycled through (0 = enough for >= 1 GB of KV)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "api.cpp"):
+        with open(os.path.join(ROOT, "paged_kv_cache_266_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the partition kernel from the committed counter
+    summary, or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(case, min_seconds: float):
+    import oracle
+
+    threads = oracle.default_threads()
+    oracle.paged_decode(case, n_threads=threads)          # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_decode(case, n_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(case.bytes_alg() * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the whole {case.cfg.name} workload (seed {case.seed}), "
+                  f"{reps} fp64 layer-steps in {el:.1f} s, {el / reps * 1e6:.0f} us per layer-step; "
+                  f"{cpu_model}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+    from synth import CONFIGS, make_case
+    from synth.device import upload
+    import ctypes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L = lib()
+    cfg = CONFIGS[args.config]
+    case = make_case(cfg)
+    bytes_alg = case.bytes_alg()
+
+    # block tables through the library's own allocator, as a caller would
+    with pkv.KVPool(cfg.num_pages, cfg.page_size, initial_free_order=case.free_order) as pool:
+        for b, n in enumerate(case.context_lens):
+            pool.allocate(b, int(n))
+        bt, lens = pool.block_tables(list(range(cfg.batch)), cfg.max_blocks)
+    assert (bt == case.block_tables).all() and (lens == case.context_lens).all()
+
+    kv_bytes_layer = case.total_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * (1 if cfg.kv_dtype == "i8" else 2)
+    rotate = args.rotate or max(1, -(-(1 << 30) // max(kv_bytes_layer, 1)))
+    layers = [upload(case, "cuda") for _ in range(rotate)]
+    q = layers[0].q
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    argv = []
+    for dev in layers:
+        a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens,
+                            case.scale, max_context_len=cfg.max_context_len, out=out,
+                            k_scale=dev.k_scale, v_scale=dev.v_scale,
+                            partition_tokens=args.partition_tokens)
+        argv.append(a)
+    ws = pkv.alloc_workspace(argv[0], q.device)
+    for a in argv:
+        a.workspace = 0 if ws is None else ws.data_ptr()
+        a.workspace_bytes = 0 if ws is None else ws.numel()
+    T = L.pkv_decode_partition_tokens(ctypes.byref(argv[0]))
+    multi = cfg.max_context_len > T
+
+    def step(i, ev=None):
+        a = ctypes.byref(argv[i % rotate])
+        if ev is not None:
+            ev[0].record(stream)
+        check(L.pkv_paged_attn_decode_partitions(a, sh))
+        if ev is not None:
+            ev[1].record(stream)
+        if multi:
+            check(L.pkv_splitk_reduce(a, sh))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # parity of the benchmarked launch configuration against the oracle
+    import oracle
+
+    got = out.to(torch.float64).cpu().numpy()
+    ref = oracle.paged_decode(case)
+    max_err = float(np.abs(got - ref).max())
+    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}[cfg.kv_dtype]
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+
+    part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    red_ms = step_ms - part_ms
+    ms_per_step = wall_ms / args.steps
+    value = bytes_alg / (ms_per_step * 1e-3) / 1e9
+
+    achieved = bytes_alg / (part_ms.mean() * 1e-3) / 1e9
+    traffic = traffic_from_profile(cfg.name)
+    result = {
+        "metric": "paged-attn decode HBM GB/s (% of 8 TB/s peak), us per layer-step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "batch": cfg.batch, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "page_size": cfg.page_size, "q_dtype": cfg.q_dtype,
+            "kv_dtype": cfg.kv_dtype, "context_tokens": case.total_tokens,
+            "max_context_len": cfg.max_context_len, "partition_tokens": T,
+            "layers_rotated": rotate, "seed": cfg.seed, "bytes_alg_per_step": bytes_alg,
+        },
+        "us_per_layer_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "event_us": {
+            "step_median": round(float(np.median(step_ms)) * 1e3, 2),
+            "step_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+            "step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+            "partition_kernel_mean": round(float(part_ms.mean()) * 1e3, 2),
+            "reduce_kernel_mean": round(float(red_ms.mean()) * 1e3, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel (partition kernel)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "parity": {"max_abs_err": max_err, "tol": tol, "ok": bool(max_err <= tol)},
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+/*
+ * libpagedkv -- single-token decode attention over a paged KV cache, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The problem statement these calls follow:
+ *
+ *  - "TensorRT-LLM 深度实战：从 Blackwell 架构到 INT4 量化的 LLM 推理性能革命"
+ *    (chenxutan.com), section 3.1 "Paged KV Cache": a pool of fixed-size
+ *    pages, a free-page list, a per-sequence page table, allocate /
+ *    append_tokens / release, and an out-of-memory error when the free list
+ *    runs dry;
+ *  - the same page, section 3.3 "融合 CUDA Kernel": the attention a decode
+ *    step computes -- scores scale * q.k, max-subtracted softmax, softmax-
+ *    weighted sum of V -- fused so that K and V are read once and the output
+ *    written once;
+ *  - "TensorRT-LLM 推理加速实战：从 engine 编译到 kernel 调优"
+ *    (socake.github.io), section 7.2 (masked_mha: decode attention for one
+ *    new token per sequence per step), section 8 (block sizes 64 and 16) and
+ *    section 8.1 (KV size = 2 x layers x kv_heads x head_dim x bytes per
+ *    token, with grouped KV heads);
+ *  - the aiqz.cc TensorRT-LLM explainer, section "KV缓存管理" (the total
+ *    M_kv = 2 x layers x heads x d_head x tokens x batch x bytes, and paging
+ *    of the KV memory).
+ *
+ * Conventions shared by every call:
+ *  - Every call returns pkv_status: PKV_OK (0) or a negative error code.  On
+ *    error nothing observable has changed, and pkv_last_error() returns a
+ *    message for the calling thread.
+ *  - "host" pointers are CPU memory owned by the caller, read or written only
+ *    during the call.  "device" pointers are GPU memory owned by the caller
+ *    (for instance torch tensors); the library never allocates, frees or
+ *    retains them.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and is asynchronous: the call returns after launching.  Launch
+ *    failures are PKV_ERR_DEVICE.
+ *  - Layouts are dense, row-major, with no padding:
+ *      q, out        [batch][num_q_heads][head_dim]
+ *      k_pool/v_pool [num_pages][num_kv_heads][page_size][head_dim]
+ *      k/v_scale     [num_pages][num_kv_heads][page_size]     (fp32, int8 only)
+ *      block_tables  [batch][max_blocks]                      (int32)
+ *      context_lens  [batch]                                  (int32)
+ *    One page id addresses the same page in every layer's pools; block
+ *    tables are shared by all layers.
+ *  - Query head h reads KV head h / (num_q_heads / num_kv_heads): query heads
+ *    share KV heads in contiguous groups (GQA; MQA when num_kv_heads == 1).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned buffer  */
+    PKV_ERR_OOM = -2,         /* the free-page list cannot cover a request  */
+    PKV_ERR_NO_SEQ = -3,      /* unknown sequence id                        */
+    PKV_ERR_SEQ_EXISTS = -4,  /* sequence id already allocated              */
+    PKV_ERR_UNSUPPORTED = -5, /* shape / dtype outside the compiled set     */
+    PKV_ERR_WORKSPACE = -6,   /* workspace missing or too small             */
+    PKV_ERR_DEVICE = -7       /* HIP runtime error (no device, bad launch)  */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F16 = 0,  /* IEEE binary16                                          */
+    PKV_BF16 = 1, /* bfloat16                                               */
+    PKV_I8 = 2    /* symmetric int8 code; value = fp32 scale x code, one
+                     scale per (page, kv head, slot), i.e. per token per head */
+} pkv_dtype;
+
+int32_t pkv_abi_version(void);
+const char *pkv_status_string(pkv_status status);
+/* Message describing the last error raised on the calling thread ("" if none). */
+const char *pkv_last_error(void);
+/* Number of visible HIP devices (0 when there is none or the runtime fails). */
+int32_t pkv_device_count(void);
+
+/* ===================================================================== *
+ * Host page pool (section 3.1 of the first page).  Pure host bookkeeping:
+ * it hands out page ids; the K/V bytes live in caller-owned device pools.
+ * A pool handle is not thread-safe: use it from one thread at a time.
+ * ===================================================================== */
+
+typedef struct pkv_pool pkv_pool;
+
+typedef struct pkv_pool_desc {
+    int32_t num_pages;                  /* > 0                                     */
+    int32_t page_size;                  /* tokens per page, > 0 (16 and 64 are
+                                           the sizes the decode kernel supports)   */
+    const int32_t *initial_free_order;  /* host, num_pages entries, a permutation
+                                           of [0, num_pages); NULL = 0, 1, ..., n-1.
+                                           Pages are taken from the END of the list
+                                           and released pages are pushed back onto
+                                           its end, in the sequence's page order.  */
+} pkv_pool_desc;
+
+/* Creates a pool.  *out receives the handle (host memory owned by the
+ * library until pkv_pool_destroy).  INVALID_ARG on a bad descriptor. */
+pkv_status pkv_pool_create(const pkv_pool_desc *desc, pkv_pool **out);
+void pkv_pool_destroy(pkv_pool *pool);
+
+/* Admits sequence seq_id holding num_tokens tokens: takes
+ * ceil(num_tokens / page_size) pages, all or nothing.  OOM if the free list
+ * is too short, SEQ_EXISTS if seq_id is live; neither changes the pool.
+ * slots_out (host, may be NULL) receives num_tokens slot ids
+ * page * page_size + offset, in token order. */
+pkv_status pkv_seq_alloc(pkv_pool *pool, int64_t seq_id, int32_t num_tokens,
+                         int64_t *slots_out);
+
+/* Adds n_new tokens to a live sequence, taking
+ * ceil((count + n_new - capacity) / page_size) new pages when the current
+ * pages overflow.  OOM (checked before any page is taken) or NO_SEQ leave the
+ * pool unchanged.  slots_out (host, may be NULL) receives the n_new slot ids
+ * of the new tokens. */
+pkv_status pkv_append_tokens(pkv_pool *pool, int64_t seq_id, int32_t n_new,
+                             int64_t *slots_out);
+
+/* Retires a sequence and pushes its pages back onto the free list.  NO_SEQ
+ * for an unknown id. */
+pkv_status pkv_seq_release(pkv_pool *pool, int64_t seq_id);
+
+/* Token and page count of a live sequence (either output may be NULL). */
+pkv_status pkv_seq_info(const pkv_pool *pool, int64_t seq_id, int32_t *num_tokens,
+                        int32_t *num_pages);
+
+/* Copies a live sequence's page ids, in logical order, into pages_out (host,
+ * capacity entries); *n_pages receives the count.  INVALID_ARG if capacity is
+ * too small. */
+pkv_status pkv_seq_pages(const pkv_pool *pool, int64_t seq_id, int32_t *pages_out,
+                         int32_t capacity, int32_t *n_pages);
+
+int32_t pkv_free_page_count(const pkv_pool *pool);
+
+/* Copies the free list, bottom to top (the next page handed out is the last
+ * entry), into out (host, capacity entries); *count receives its length. */
+pkv_status pkv_free_pages(const pkv_pool *pool, int32_t *out, int32_t capacity,
+                          int32_t *count);
+
+/* Writes the block tables and context lengths of `batch` live sequences:
+ * block_tables_out (host, [batch][max_blocks]) gets each sequence's page ids
+ * followed by -1 padding; context_lens_out (host, [batch]) its token count.
+ * NO_SEQ for an unknown id, INVALID_ARG if a sequence has more than
+ * max_blocks pages. */
+pkv_status pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids,
+                                  int32_t batch, int32_t max_blocks,
+                                  int32_t *block_tables_out, int32_t *context_lens_out);
+
+/* KV-cache bytes 2 x layers x kv_heads x head_dim x tokens x batch x bytes(dtype)
+ * (section 8.1 of the engine-to-kernel-tuning page; the M_kv equation of the
+ * aiqz.cc explainer).  int8 counts the codes only (scales excluded).
+ * Returns -1 for a negative argument or overflow. */
+int64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_t tokens,
+                     int32_t batch, pkv_dtype dtype);
+
+/* ===================================================================== *
+ * Device: decode attention (section 3.3 of the first page; masked_mha of
+ * section 7.2 of the engine-to-kernel-tuning page).
+ * ===================================================================== */
+
+typedef struct pkv_decode_args {
+    const void *q;              /* device [batch][num_q_heads][head_dim], q_dtype   */
+    const void *k_pool;         /* device [num_pages][num_kv_heads][page_size][head_dim] */
+    const void *v_pool;         /* device, same shape                                */
+    const float *k_scale;       /* device [num_pages][num_kv_heads][page_size]; int8
+                                   KV only, otherwise NULL                           */
+    const float *v_scale;
+    const int32_t *block_tables;/* device [batch][max_blocks]; entry j of row b is the
+                                   physical page of tokens [j*page_size, (j+1)*page_size)
+                                   of sequence b.  Entries j >= ceil(len_b/page_size)
+                                   are never read.                                   */
+    const int32_t *context_lens;/* device [batch]: tokens in the cache for each
+                                   sequence, including the one just appended; the
+                                   single query attends to all of them.             */
+    void *out;                  /* device [batch][num_q_heads][head_dim], q_dtype    */
+    void *workspace;            /* device scratch of >= pkv_decode_workspace_bytes;
+                                   may be NULL when that size is 0                  */
+    size_t workspace_bytes;
+    int32_t batch;              /* >= 0; 0 is a no-op                               */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;       /* divides num_q_heads; group = Hq / Hkv in {1,2,4,8} */
+    int32_t head_dim;           /* 64 or 128                                        */
+    int32_t page_size;          /* 16 or 64                                         */
+    int32_t num_pages;          /* pages in each pool                               */
+    int32_t max_blocks;         /* row length of block_tables                       */
+    int32_t max_context_len;    /* host bound on every context_lens entry;
+                                   <= max_blocks * page_size                         */
+    int32_t partition_tokens;   /* split-K partition length; 0 = library default.
+                                   Otherwise a positive multiple of 64.              */
+    pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16; out has the same type       */
+    pkv_dtype kv_dtype;         /* PKV_F16 (with f16 q), PKV_BF16 (with bf16 q), or
+                                   PKV_I8 (with either)                              */
+    float scale;                /* softmax scale applied to q.k (e.g. 1/sqrt(head_dim)) */
+} pkv_decode_args;
+
+/* Bytes of workspace pkv_paged_attn_decode needs for these arguments (uses
+ * batch, num_q_heads, head_dim, max_context_len, partition_tokens).  Zero when
+ * every sequence fits one partition. */
+pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *args, size_t *bytes);
+
+/* Partition length the library uses for these arguments (resolves 0). */
+int32_t pkv_decode_partition_tokens(const pkv_decode_args *args);
+
+/* Checks the arguments without touching the GPU (pointer presence and
+ * 16-byte alignment, shapes, dtype pair, workspace size).  Returns what
+ * pkv_paged_attn_decode would return before launching. */
+pkv_status pkv_decode_validate(const pkv_decode_args *args);
+
+/* out[b][h][:] = softmax_t(scale * q[b][h] . K_t) . V_t over the
+ * context_lens[b] cached tokens of sequence b, read through block_tables from
+ * KV head h / group.  Sequences with context length 0 get zeros.  A sequence
+ * whose context length is negative or above max_context_len, or whose block
+ * table names a page outside [0, num_pages), gets NaN in every element of its
+ * output instead of a memory access outside the pools.
+ * Long sequences are split into partitions of partition_tokens tokens whose
+ * partial results are merged by a second kernel (two launches on `stream`).
+ * Stateless and re-entrant; the workspace must not be shared by concurrent
+ * calls. */
+pkv_status pkv_paged_attn_decode(const pkv_decode_args *args, void *stream);
+
+/* The two launches of pkv_paged_attn_decode, separately (same arguments and
+ * workspace): the partition kernel writes the output of single-partition
+ * sequences and the partials of the others; the reduce kernel merges those
+ * partials.  Calling both in order on one stream is pkv_paged_attn_decode. */
+pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *args, void *stream);
+pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
+
+/* ===================================================================== *
+ * Device: write appended tokens' K/V into their slots (the device side of
+ * append_tokens, section 3.1 of the first page).
+ * ===================================================================== */
+
+typedef struct pkv_write_args {
+    const void *k_new;          /* device [n][num_kv_heads][head_dim], kv_dtype      */
+    const void *v_new;
+    const float *k_scale_new;   /* device [n][num_kv_heads] fp32; int8 only, else NULL */
+    const float *v_scale_new;
+    const int64_t *slots;       /* device [n]: page * page_size + offset, as returned by
+                                   pkv_seq_alloc / pkv_append_tokens.  A slot outside
+                                   [0, num_pages * page_size) is skipped.            */
+    void *k_pool;               /* device pools, as in pkv_decode_args               */
+    void *v_pool;
+    float *k_scale;             /* device pool scales; int8 only, else NULL          */
+    float *v_scale;
+    int32_t n;                  /* tokens to write, >= 0                             */
+    int32_t num_kv_heads;
+    int32_t head_dim;           /* 64 or 128                                        */
+    int32_t page_size;
+    int32_t num_pages;
+    pkv_dtype kv_dtype;
+} pkv_write_args;
+
+pkv_status pkv_write_kv(const pkv_write_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

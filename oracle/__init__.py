@@ -83,10 +83,16 @@ def set_lib(L):
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when that is set."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _ptr(a: Optional[np.ndarray], ctype):

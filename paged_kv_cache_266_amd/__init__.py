@@ -1,0 +1,12 @@
+"""libpagedkv: single-token decode attention over a paged KV cache, MI355X.
+
+Python face of the C library (include/pagedkv.h).  The library is loaded on
+first use; if it has not been built, that first use raises -- nothing here
+computes attention itself.
+"""
+
+from ._lib import (KVCacheOOM, PagedKVError, SequenceExists, Unsupported,  # noqa: F401
+                   UnknownSequence, WorkspaceError, DeviceError, lib)
+from .pool import KVPool, kv_bytes  # noqa: F401
+from .ops import (alloc_workspace, decode_args, paged_attn_decode,  # noqa: F401
+                  workspace_bytes, write_kv)

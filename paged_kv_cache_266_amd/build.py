@@ -1,0 +1,72 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+``python -m paged_kv_cache_266_amd.build`` (or ``build()``) always
+recompiles.  Each translation unit is compiled to an object in parallel and
+linked into ``paged_kv_cache_266_amd/libpagedkv.so``.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from typing import List, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libpagedkv.so")
+ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
+SOURCES = ["decode.hip", "api.cpp", "pool.cpp"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def common_flags() -> List[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # no packed-FP32 instructions anywhere in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{os.path.join(ROOT, 'include')}",
+    ]
+
+
+def _compile(src: str, obj: str, extra: List[str]) -> str:
+    cmd = [hipcc(), *common_flags(), *extra, "-c", "-x", "hip", src, "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build(verbose: bool = False, extra_flags: Optional[List[str]] = None) -> str:
+    extra = list(extra_flags or [])
+    with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
+        objs = []
+        with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(tmp, s + ".o"), extra)
+                    for s in SOURCES]
+            for f in futs:
+                objs.append(f.result())
+        tmp_lib = LIB + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        os.replace(tmp_lib, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra_flags=sys.argv[1:])

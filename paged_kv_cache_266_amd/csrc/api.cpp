@@ -1,0 +1,271 @@
+// C ABI entry points of libpagedkv for the device side: argument validation,
+// choice of kernel instantiation and partitioning, launches.
+//
+// The decode step is the masked_mha role of "TensorRT-LLM 推理加速实战"
+// (socake.github.io), section 7.2, computing the fused attention of
+// "TensorRT-LLM 深度实战" (chenxutan.com), section 3.3, over K/V reached
+// through the page tables of section 3.1 of the same page.  Long contexts are
+// cut into partitions whose partial softmax statistics a second kernel merges
+// (the >128k-token contexts of "TensorRT-LLM 核心架构解析", section 1.2, would
+// otherwise leave most of the GPU idle with one workgroup per head).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+void clear_error() { g_last_error.clear(); }
+
+pkv_status fail(pkv_status code, const char *msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static pkv_status device_fail(int err, const char *where)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s: %s", where, hipGetErrorString((hipError_t)err));
+    g_last_error = buf;
+    return PKV_ERR_DEVICE;
+}
+
+static int32_t resolve_partition(const pkv_decode_args *a)
+{
+    return a->partition_tokens > 0 ? a->partition_tokens : kDefaultPartitionTokens;
+}
+
+static int32_t num_partitions(const pkv_decode_args *a)
+{
+    int32_t T = resolve_partition(a);
+    int32_t P = (a->max_context_len + T - 1) / T;
+    return P < 1 ? 1 : P;
+}
+
+static size_t workspace_bytes(const pkv_decode_args *a)
+{
+    int32_t P = num_partitions(a);
+    if (P <= 1 || a->batch == 0)
+        return 0;
+    size_t units = (size_t)a->batch * (size_t)a->num_q_heads * (size_t)P;
+    size_t o = units * (size_t)a->head_dim * sizeof(float);
+    size_t ml = units * 2 * sizeof(float);
+    return ((o + 255) & ~(size_t)255) + ml;
+}
+
+// Shape, dtype and pointer checks; no GPU access.
+static pkv_status validate(const pkv_decode_args *a)
+{
+    if (!a)
+        return fail(PKV_ERR_INVALID_ARG, "decode: null argument struct");
+    if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->num_pages <= 0 ||
+        a->max_blocks < 0 || a->max_context_len < 0)
+        return fail(PKV_ERR_INVALID_ARG, "decode: sizes must be positive (batch, max_blocks, "
+                                         "max_context_len non-negative)");
+    if (a->num_q_heads % a->num_kv_heads)
+        return fail(PKV_ERR_INVALID_ARG, "decode: num_kv_heads must divide num_q_heads");
+    if ((int64_t)a->max_context_len > (int64_t)a->max_blocks * a->page_size)
+        return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len exceeds max_blocks * page_size");
+    if (a->partition_tokens < 0 || a->partition_tokens % kTileTokens)
+        return fail(PKV_ERR_INVALID_ARG, "decode: partition_tokens must be 0 or a positive multiple of 64");
+    bool kv_ok = (a->kv_dtype == PKV_I8 && (a->q_dtype == PKV_F16 || a->q_dtype == PKV_BF16)) ||
+                 (a->kv_dtype == PKV_F16 && a->q_dtype == PKV_F16) ||
+                 (a->kv_dtype == PKV_BF16 && a->q_dtype == PKV_BF16);
+    int group = a->num_q_heads / a->num_kv_heads;
+    if (!kv_ok || !decode_instantiated(a->head_dim, a->page_size, group, a->q_dtype, a->kv_dtype))
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "decode: supported set is head_dim {64,128}, page_size {16,64}, group {1,2,4,8}, "
+                    "(q,kv) in {(f16,f16),(bf16,bf16),(f16,i8),(bf16,i8)}");
+    if (a->batch == 0)
+        return PKV_OK;
+    if (!a->q || !a->k_pool || !a->v_pool || !a->block_tables || !a->context_lens || !a->out)
+        return fail(PKV_ERR_INVALID_ARG, "decode: null device pointer");
+    if (a->kv_dtype == PKV_I8 && (!a->k_scale || !a->v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "decode: int8 KV needs k_scale and v_scale");
+    if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->out) ||
+        ((uintptr_t)a->k_scale & 3u) || ((uintptr_t)a->v_scale & 3u) ||
+        ((uintptr_t)a->block_tables & 3u) || ((uintptr_t)a->context_lens & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "decode: q, pools and out must be 16-byte aligned, "
+                                         "scales and int32 arrays 4-byte aligned");
+    size_t need = workspace_bytes(a);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need || ((uintptr_t)a->workspace & 255u)))
+        return fail(PKV_ERR_WORKSPACE, "decode: workspace missing, smaller than "
+                                       "pkv_decode_workspace_bytes, or not 256-byte aligned");
+    return PKV_OK;
+}
+
+static DecodeParams make_params(const pkv_decode_args *a)
+{
+    DecodeParams p{};
+    p.q = a->q;
+    p.k_pool = a->k_pool;
+    p.v_pool = a->v_pool;
+    p.k_scale = a->k_scale;
+    p.v_scale = a->v_scale;
+    p.block_tables = a->block_tables;
+    p.context_lens = a->context_lens;
+    p.out = a->out;
+    p.batch = a->batch;
+    p.num_q_heads = a->num_q_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.num_pages = a->num_pages;
+    p.max_blocks = a->max_blocks;
+    p.max_context_len = a->max_context_len;
+    p.partition_tokens = resolve_partition(a);
+    p.num_partitions = num_partitions(a);
+    // log2(e) folded into the scale once, in fp32, so the kernels use exp2
+    p.scale_log2 = a->scale * 1.44269504088896340736f;
+    if (workspace_bytes(a) > 0) {
+        size_t units = (size_t)a->batch * (size_t)a->num_q_heads * (size_t)p.num_partitions;
+        size_t o = units * (size_t)a->head_dim * sizeof(float);
+        p.part_o = (float *)a->workspace;
+        p.part_ml = (float *)((char *)a->workspace + ((o + 255) & ~(size_t)255));
+    }
+    return p;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+extern "C" const char *pkv_status_string(pkv_status s)
+{
+    switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_OOM: return "out of KV pages";
+    case PKV_ERR_NO_SEQ: return "unknown sequence";
+    case PKV_ERR_SEQ_EXISTS: return "sequence already exists";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+extern "C" const char *pkv_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int32_t pkv_device_count(void)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess)
+        return 0;
+    return n;
+}
+
+extern "C" pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *a, size_t *bytes)
+{
+    clear_error();
+    if (!a || !bytes)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: null argument");
+    if (a->batch < 0 || a->num_q_heads <= 0 || a->max_context_len < 0 || a->partition_tokens < 0 ||
+        a->partition_tokens % kTileTokens || a->head_dim <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: bad sizes");
+    *bytes = workspace_bytes(a);
+    return PKV_OK;
+}
+
+extern "C" int32_t pkv_decode_partition_tokens(const pkv_decode_args *a)
+{
+    return a ? resolve_partition(a) : 0;
+}
+
+extern "C" pkv_status pkv_decode_validate(const pkv_decode_args *a)
+{
+    clear_error();
+    return validate(a);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *a, void *stream)
+{
+    clear_error();
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->batch == 0)
+        return st;
+    DecodeParams p = make_params(a);
+    int err = launch_decode_partitions(p, a->head_dim, a->page_size, a->num_q_heads / a->num_kv_heads,
+                                       a->q_dtype, a->kv_dtype, stream);
+    return err ? device_fail(err, "pkv_paged_attn_decode_partitions") : PKV_OK;
+}
+
+extern "C" pkv_status pkv_splitk_reduce(const pkv_decode_args *a, void *stream)
+{
+    clear_error();
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->batch == 0)
+        return st;
+    DecodeParams p = make_params(a);
+    if (p.num_partitions <= 1)
+        return PKV_OK;
+    int err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
+    return err ? device_fail(err, "pkv_splitk_reduce") : PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_attn_decode(const pkv_decode_args *a, void *stream)
+{
+    clear_error();
+    pkv_status st = validate(a);
+    if (st != PKV_OK || a->batch == 0)
+        return st;
+    DecodeParams p = make_params(a);
+    int err = launch_decode_partitions(p, a->head_dim, a->page_size, a->num_q_heads / a->num_kv_heads,
+                                       a->q_dtype, a->kv_dtype, stream);
+    if (err)
+        return device_fail(err, "pkv_paged_attn_decode (partition kernel)");
+    if (p.num_partitions > 1) {
+        err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
+        if (err)
+            return device_fail(err, "pkv_paged_attn_decode (reduce kernel)");
+    }
+    return PKV_OK;
+}
+
+extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)
+{
+    clear_error();
+    if (!a)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: null argument struct");
+    if (a->n < 0 || a->num_kv_heads <= 0 || a->page_size <= 0 || a->num_pages <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: bad sizes");
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: head_dim must be 64 or 128");
+    if (a->kv_dtype != PKV_F16 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_I8)
+        return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: unknown kv dtype");
+    if (a->n == 0)
+        return PKV_OK;
+    if (!a->k_new || !a->v_new || !a->slots || !a->k_pool || !a->v_pool)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: null device pointer");
+    bool i8 = a->kv_dtype == PKV_I8;
+    if (i8 && (!a->k_scale_new || !a->v_scale_new || !a->k_scale || !a->v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: int8 KV needs the four scale pointers");
+    if (!aligned16(a->k_new) || !aligned16(a->v_new) || !aligned16(a->k_pool) || !aligned16(a->v_pool) ||
+        ((uintptr_t)a->slots & 7u))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: K/V buffers must be 16-byte aligned, slots 8-byte");
+    WriteParams p{};
+    p.k_new = a->k_new;
+    p.v_new = a->v_new;
+    p.k_scale_new = i8 ? a->k_scale_new : nullptr;
+    p.v_scale_new = i8 ? a->v_scale_new : nullptr;
+    p.slots = a->slots;
+    p.k_pool = a->k_pool;
+    p.v_pool = a->v_pool;
+    p.k_scale = i8 ? a->k_scale : nullptr;
+    p.v_scale = i8 ? a->v_scale : nullptr;
+    p.n = a->n;
+    p.num_kv_heads = a->num_kv_heads;
+    p.page_size = a->page_size;
+    p.num_pages = a->num_pages;
+    p.row_bytes = a->head_dim * (i8 ? 1 : 2);
+    int err = launch_write_kv(p, stream);
+    return err ? device_fail(err, "pkv_write_kv") : PKV_OK;
+}

@@ -1,0 +1,71 @@
+// Internal declarations shared by the host-side translation units of
+// libpagedkv.  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+// Thread-local error message behind pkv_last_error().
+void clear_error();
+pkv_status fail(pkv_status code, const char *msg);
+
+// Tokens per wave-iteration of the decode kernel and waves per workgroup.
+constexpr int kTileTokens = 64;
+constexpr int kWaves = 4;
+constexpr int kDefaultPartitionTokens = 512;
+
+enum DType : int { F16 = 0, BF16 = 1, I8 = 2 };
+
+// Everything the decode kernels read; built by the host from pkv_decode_args.
+struct DecodeParams {
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    void *out;
+    float *part_o;     // [batch][Hq][P][D]
+    float *part_ml;    // [batch][Hq][P][2]: (max in log2 units, sum)
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_pages;
+    int32_t max_blocks;
+    int32_t max_context_len;
+    int32_t partition_tokens;
+    int32_t num_partitions;
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+struct WriteParams {
+    const void *k_new;
+    const void *v_new;
+    const float *k_scale_new;
+    const float *v_scale_new;
+    const int64_t *slots;
+    void *k_pool;
+    void *v_pool;
+    float *k_scale;
+    float *v_scale;
+    int32_t n;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t row_bytes;
+};
+
+// Kernel launchers (device code lives in the .hip translation units).
+// Each returns a hipError_t value as int (0 = success).
+bool decode_instantiated(int head_dim, int page_size, int group, int q_dtype, int kv_dtype);
+int launch_decode_partitions(const DecodeParams &p, int head_dim, int page_size, int group,
+                             int q_dtype, int kv_dtype, void *stream);
+int launch_splitk_reduce(const DecodeParams &p, int head_dim, int q_dtype, void *stream);
+int launch_write_kv(const WriteParams &p, void *stream);
+
+}  // namespace pkv

@@ -1,0 +1,149 @@
+"""Decode attention and K/V writes on torch tensors, through libpagedkv.
+
+These functions only marshal arguments: tensor data pointers, sizes and the
+current HIP stream go to the C ABI, and every step runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from ._lib import DTYPE_CODES, DecodeArgs, WriteArgs, check, lib
+
+
+def _dtype_name(t) -> str:
+    import torch
+
+    m = {torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _check_tensor(t, name, device, ndim=None):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def decode_args(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
+                max_context_len: int, out=None, k_scale=None, v_scale=None,
+                workspace=None, partition_tokens: int = 0) -> DecodeArgs:
+    """Fill the C argument struct from tensors (no device work)."""
+    import torch
+
+    device = q.device
+    for t, n, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4),
+                     (block_tables, "block_tables", 2), (context_lens, "context_lens", 1),
+                     (out, "out", 3), (k_scale, "k_scale", 3), (v_scale, "v_scale", 3)):
+        _check_tensor(t, n, device, nd)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    B, Hq, D = q.shape
+    num_pages, Hkv, PS, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shape does not match q")
+    a = DecodeArgs()
+    a.q, a.k_pool, a.v_pool = _ptr(q), _ptr(k_pool), _ptr(v_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.block_tables, a.context_lens = _ptr(block_tables), _ptr(context_lens)
+    a.out = _ptr(out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = B, Hq, Hkv, D
+    a.page_size, a.num_pages = PS, num_pages
+    a.max_blocks = block_tables.shape[1]
+    a.max_context_len = int(max_context_len)
+    a.partition_tokens = int(partition_tokens)
+    a.q_dtype = DTYPE_CODES[_dtype_name(q)]
+    a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
+    a.scale = float(scale)
+    return a
+
+
+def workspace_bytes(args: DecodeArgs) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pkv_decode_workspace_bytes(ctypes.byref(args), ctypes.byref(n)), "workspace_bytes")
+    return int(n.value)
+
+
+def alloc_workspace(args: DecodeArgs, device):
+    """A workspace tensor for these arguments (None when none is needed)."""
+    import torch
+
+    n = workspace_bytes(args)
+    if n == 0:
+        return None
+    # torch's caching allocator hands out 512-byte aligned blocks
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
+                      max_context_len: int, out=None, k_scale=None, v_scale=None,
+                      workspace=None, partition_tokens: int = 0, stream=None):
+    """Single-token decode attention over a paged KV cache.
+
+    q [B][Hq][D] f16/bf16; k_pool, v_pool [num_pages][Hkv][PS][D] of the same
+    type as q or int8 (then k_scale, v_scale [num_pages][Hkv][PS] fp32);
+    block_tables [B][max_blocks] int32; context_lens [B] int32 (device).
+    ``max_context_len`` is a host-side bound on context_lens (it sizes the
+    split-K grid).  Returns ``out`` [B][Hq][D] in q's dtype.
+    """
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q)
+    a = decode_args(q, k_pool, v_pool, block_tables, context_lens, scale,
+                    max_context_len=max_context_len, out=out, k_scale=k_scale, v_scale=v_scale,
+                    workspace=workspace, partition_tokens=partition_tokens)
+    if workspace is None:
+        workspace = alloc_workspace(a, q.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = 0 if workspace is None else workspace.numel()
+    check(lib().pkv_paged_attn_decode(ctypes.byref(a), _stream_handle(stream, q.device)),
+          "paged_attn_decode")
+    return out
+
+
+def write_kv(k_new, v_new, slots, k_pool, v_pool, *, k_scale_new=None, v_scale_new=None,
+             k_scale=None, v_scale=None, stream=None) -> None:
+    """Scatter appended tokens' K/V ([n][Hkv][D]) into their pool slots."""
+    import torch
+
+    device = k_pool.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slots, "slots"), (k_pool, "k_pool"),
+                 (v_pool, "v_pool"), (k_scale_new, "k_scale_new"), (v_scale_new, "v_scale_new"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check_tensor(t, n, device)
+    if slots.dtype != torch.int64:
+        raise TypeError("slots must be int64")
+    num_pages, Hkv, PS, D = k_pool.shape
+    a = WriteArgs()
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+    a.k_scale_new, a.v_scale_new = _ptr(k_scale_new), _ptr(v_scale_new)
+    a.slots = _ptr(slots)
+    a.k_pool, a.v_pool = _ptr(k_pool), _ptr(v_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.n = k_new.shape[0]
+    a.num_kv_heads, a.head_dim, a.page_size, a.num_pages = Hkv, D, PS, num_pages
+    a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
+    check(lib().pkv_write_kv(ctypes.byref(a), _stream_handle(stream, device)), "write_kv")

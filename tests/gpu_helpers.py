@@ -1,0 +1,61 @@
+"""Shared pieces of the GPU parity tests: run the HIP path on a generated
+workload and compare it with the fp64 oracle."""
+
+import sys
+
+import numpy as np
+
+import oracle
+from synth import get_config, make_case
+from synth.device import upload
+
+# max-abs tolerances on outputs, by KV storage type
+TOL = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def small_config(Hq, Hkv, D, qd, kvd, PS, lens, num_pages=None):
+    pages = sum(-(-n // PS) for n in lens)
+    return get_config("tiny", batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      q_dtype=qd, kv_dtype=kvd, page_size=PS,
+                      num_pages=num_pages or max(2 * pages, 16),
+                      lens_kind="fixed", lens_args=tuple(lens))
+
+
+def gpu_decode(case, partition_tokens=0, dev=None, max_context_len=None):
+    """Run pkv_paged_attn_decode on the case; returns the output tensor."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    cfg = case.cfg
+    dev = dev or upload(case, "cuda")
+    mcl = cfg.max_context_len if max_context_len is None else max_context_len
+    out = pkv.paged_attn_decode(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens,
+                                case.scale, max_context_len=mcl, k_scale=dev.k_scale,
+                                v_scale=dev.v_scale, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def to_f64(t):
+    import torch
+
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def compare(case, got, label=""):
+    ref = oracle.paged_decode(case)
+    g = to_f64(got)
+    assert np.isfinite(g).all(), f"{label}: non-finite output"
+    err = np.abs(g - ref)
+    tol = TOL[case.cfg.kv_dtype]
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    note(f"  {label}: max|err| {err.max():.3e} at {tuple(int(i) for i in worst)}, "
+         f"rms {np.sqrt((err ** 2).mean()):.3e}, tol {tol}")
+    assert err.max() <= tol, f"{label}: max |gpu - oracle| = {err.max()} > {tol}"
+    return err.max()
