@@ -28,8 +28,9 @@
 //    dots.  A DPP reduce-scatter over the R lanes of a row leaves each lane
 //    with the full scores of ONE token (token r + (64/R) j of the tile) for
 //    all G heads -- no redundant softmax work.
-//  * Online softmax.  Tile max per head by DPP row rotations plus
-//    permlane16/32 swaps; running max, per-lane running sums, exp2 with
+//  * Online softmax.  Tile max per head by DPP row rotations and a
+//    wave-uniform combine of the four rows; running max, per-lane running
+//    sums, exp2 with
 //    log2(e) folded into the scale.  For int8, the V scale of the token is
 //    folded into its probability and the K scale into its score.
 //  * p.V.  Probabilities go to a per-wave LDS slot; each lane then reads, per
@@ -79,30 +80,11 @@ template <> struct Partner<1> { static constexpr int ctrl = kQuadXor2; };
 template <> struct Partner<2> { static constexpr int ctrl = kRowHalfMirror; };
 template <> struct Partner<3> { static constexpr int ctrl = kRowRor8; };
 
-// Lane l gets max/sum of its own value and that of lane l^16 / l^32.
-__device__ __forceinline__ float xor16_max(float x)
+// Full reductions over the 64 lanes.  DPP rotations finish each 16-lane row;
+// the four row results are then read as wave-uniform values.
+__device__ __forceinline__ float lane_value(float x, int lane)
 {
-    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(u32, x), __builtin_bit_cast(u32, x),
-                                              false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(u32, x), __builtin_bit_cast(u32, x),
-                                              false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x)
-{
-    auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(u32, x), __builtin_bit_cast(u32, x),
-                                              false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(u32, x), __builtin_bit_cast(u32, x),
-                                              false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 __device__ __forceinline__ float wave_max(float x)
@@ -111,7 +93,7 @@ __device__ __forceinline__ float wave_max(float x)
     x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
     x = fmaxf(x, dpp<0x122>(x));  // row_ror 2
     x = fmaxf(x, dpp<0x121>(x));  // row_ror 1
-    return xor32_max(xor16_max(x));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float x)
@@ -120,10 +102,11 @@ __device__ __forceinline__ float wave_sum(float x)
     x += dpp<0x124>(x);
     x += dpp<0x122>(x);
     x += dpp<0x121>(x);
-    return xor32_sum(xor16_sum(x));
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
-// Sum over the 64/R token rows of R lanes each (lanes with equal l % R).
+// Sum over the 64/R token rows of R lanes each (lanes with equal l % R); every
+// lane receives the total of its column.
 template <int R>
 __device__ __forceinline__ float sum_over_rows(float x)
 {
@@ -131,7 +114,9 @@ __device__ __forceinline__ float sum_over_rows(float x)
         x += dpp<kRowRor4>(x);
     if constexpr (R <= 8)
         x += dpp<kRowRor8>(x);
-    return xor32_sum(xor16_sum(x));
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
 }
 
 // One reduce-scatter step over lanes that differ in bit BIT of the column:
