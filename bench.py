@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of paged single-token decode attention on one MI355X.
 
-One step = one decode call over every sequence of one layer (the partition
-kernel, then the split-K reduce kernel when sequences span several
-partitions), on synthetic inputs already resident in HBM.  Layers are rotated
+One step = one decode call over every sequence of one layer (the decode
+kernel, whose persistent grid splits the batch's tiles evenly over its waves,
+then the merge kernel), on synthetic inputs already resident in HBM.  Layers are rotated
 (distinct pool buffers with the same contents) so the 256 MB Infinity Cache
 cannot serve a layer from the previous step.
 
@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="waves sharing the batch's tiles (0 = library default)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct layer buffers cycled through (0 = enough for >= 1 GB of KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,14 +167,13 @@ def main():
         a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens,
                             case.scale, max_context_len=cfg.max_context_len, out=out,
                             k_scale=dev.k_scale, v_scale=dev.v_scale,
-                            partition_tokens=args.partition_tokens)
+                            num_splits=args.num_splits)
         argv.append(a)
     ws = pkv.alloc_workspace(argv[0], q.device)
     for a in argv:
         a.workspace = 0 if ws is None else ws.data_ptr()
         a.workspace_bytes = 0 if ws is None else ws.numel()
-    T = L.pkv_decode_partition_tokens(ctypes.byref(argv[0]))
-    multi = cfg.max_context_len > T
+    num_splits = L.pkv_decode_num_splits(ctypes.byref(argv[0]))
 
     def step(i, ev=None):
         a = ctypes.byref(argv[i % rotate])
@@ -182,8 +182,7 @@ def main():
         check(L.pkv_paged_attn_decode_partitions(a, sh))
         if ev is not None:
             ev[1].record(stream)
-        if multi:
-            check(L.pkv_splitk_reduce(a, sh))
+        check(L.pkv_splitk_reduce(a, sh))
         if ev is not None:
             ev[2].record(stream)
 
@@ -233,7 +232,7 @@ def main():
             "batch": cfg.batch, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim, "page_size": cfg.page_size, "q_dtype": cfg.q_dtype,
             "kv_dtype": cfg.kv_dtype, "context_tokens": case.total_tokens,
-            "max_context_len": cfg.max_context_len, "partition_tokens": T,
+            "max_context_len": cfg.max_context_len, "num_splits": num_splits,
             "layers_rotated": rotate, "seed": cfg.seed, "bytes_alg_per_step": bytes_alg,
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
@@ -243,11 +242,11 @@ def main():
             "step_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
             "step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
             "partition_kernel_mean": round(float(part_ms.mean()) * 1e3, 2),
-            "reduce_kernel_mean": round(float(red_ms.mean()) * 1e3, 2),
+            "merge_kernel_mean": round(float(red_ms.mean()) * 1e3, 2),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel (partition kernel)",
+            "kernel": "paged_decode_kernel",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

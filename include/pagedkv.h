@@ -190,21 +190,26 @@ typedef struct pkv_decode_args {
     int32_t max_blocks;         /* row length of block_tables                       */
     int32_t max_context_len;    /* host bound on every context_lens entry;
                                    <= max_blocks * page_size                         */
-    int32_t partition_tokens;   /* split-K partition length; 0 = library default.
-                                   Otherwise a positive multiple of 64.              */
+    int32_t num_splits;         /* waves sharing the batch: the batch's 64-token tiles
+                                   (all sequences, all KV heads) are divided into this
+                                   many equal contiguous shares, one per wave of a
+                                   persistent grid.  0 = library default (8 per compute
+                                   unit); always capped at the number of tiles the
+                                   batch can have.                                   */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16; out has the same type       */
     pkv_dtype kv_dtype;         /* PKV_F16 (with f16 q), PKV_BF16 (with bf16 q), or
                                    PKV_I8 (with either)                              */
     float scale;                /* softmax scale applied to q.k (e.g. 1/sqrt(head_dim)) */
 } pkv_decode_args;
 
-/* Bytes of workspace pkv_paged_attn_decode needs for these arguments (uses
- * batch, num_q_heads, head_dim, max_context_len, partition_tokens).  Zero when
- * every sequence fits one partition. */
+/* Bytes of workspace pkv_paged_attn_decode needs for these arguments: one
+ * (max, sum, head_dim-vector) slot per query head for every (sequence, KV
+ * head) segment plus every wave, fp32 (uses batch, num_q_heads, num_kv_heads,
+ * head_dim, max_context_len, num_splits).  0 only for an empty batch. */
 pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *args, size_t *bytes);
 
-/* Partition length the library uses for these arguments (resolves 0). */
-int32_t pkv_decode_partition_tokens(const pkv_decode_args *args);
+/* Number of waves the library uses for these arguments (resolves 0). */
+int32_t pkv_decode_num_splits(const pkv_decode_args *args);
 
 /* Checks the arguments without touching the GPU (pointer presence and
  * 16-byte alignment, shapes, dtype pair, workspace size).  Returns what
@@ -217,16 +222,16 @@ pkv_status pkv_decode_validate(const pkv_decode_args *args);
  * whose context length is negative or above max_context_len, or whose block
  * table names a page outside [0, num_pages), gets NaN in every element of its
  * output instead of a memory access outside the pools.
- * Long sequences are split into partitions of partition_tokens tokens whose
- * partial results are merged by a second kernel (two launches on `stream`).
- * Stateless and re-entrant; the workspace must not be shared by concurrent
- * calls. */
+ * Two launches on `stream`: the decode kernel (a persistent grid of
+ * num_splits waves, each streaming an equal share of the batch's tiles; a
+ * sequence/head a wave covers whole is written directly, the pieces of one
+ * shared by several waves go to the workspace) and the merge kernel (combines
+ * pieces; writes the outputs of empty sequences).  Stateless and re-entrant;
+ * the workspace must not be shared by concurrent calls. */
 pkv_status pkv_paged_attn_decode(const pkv_decode_args *args, void *stream);
 
 /* The two launches of pkv_paged_attn_decode, separately (same arguments and
- * workspace): the partition kernel writes the output of single-partition
- * sequences and the partials of the others; the reduce kernel merges those
- * partials.  Calling both in order on one stream is pkv_paged_attn_decode. */
+ * workspace).  Calling both in order on one stream is pkv_paged_attn_decode. */
 pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *args, void *stream);
 pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
 

@@ -30,7 +30,7 @@ EXPORTED = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_alloc", "pkv_append_tokens",
     "pkv_seq_release", "pkv_seq_info", "pkv_seq_pages", "pkv_free_page_count",
     "pkv_free_pages", "pkv_build_block_tables", "pkv_kv_bytes",
-    "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_decode_validate",
+    "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_decode_validate",
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
     "pkv_write_kv",
 ]
@@ -52,7 +52,7 @@ class DecodeArgs(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("max_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
-        ("partition_tokens", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
         ("scale", ctypes.c_float),
     ]
@@ -142,8 +142,8 @@ def _declare(L):
     L.pkv_kv_bytes.argtypes = [i32, i32, i32, i64, i32, ci]
     L.pkv_decode_workspace_bytes.restype = ci
     L.pkv_decode_workspace_bytes.argtypes = [P(DecodeArgs), P(sz)]
-    L.pkv_decode_partition_tokens.restype = i32
-    L.pkv_decode_partition_tokens.argtypes = [P(DecodeArgs)]
+    L.pkv_decode_num_splits.restype = i32
+    L.pkv_decode_num_splits.argtypes = [P(DecodeArgs)]
     L.pkv_decode_validate.restype = ci
     L.pkv_decode_validate.argtypes = [P(DecodeArgs)]
     for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce"):

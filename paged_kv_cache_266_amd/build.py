@@ -32,7 +32,7 @@ def hipcc() -> str:
 
 def common_flags() -> List[str]:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # no packed-FP32 instructions anywhere in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",

@@ -1,15 +1,17 @@
 // C ABI entry points of libpagedkv for the device side: argument validation,
-// choice of kernel instantiation and partitioning, launches.
+// choice of kernel instantiation and of the work split, launches.
 //
 // The decode step is the masked_mha role of "TensorRT-LLM 推理加速实战"
 // (socake.github.io), section 7.2, computing the fused attention of
 // "TensorRT-LLM 深度实战" (chenxutan.com), section 3.3, over K/V reached
-// through the page tables of section 3.1 of the same page.  Long contexts are
-// cut into partitions whose partial softmax statistics a second kernel merges
-// (the >128k-token contexts of "TensorRT-LLM 核心架构解析", section 1.2, would
-// otherwise leave most of the GPU idle with one workgroup per head).
+// through the page tables of section 3.1 of the same page.  The batch's
+// tiles are divided evenly among a persistent grid of waves; sequences longer
+// than a wave's share -- the >128k-token contexts of "TensorRT-LLM 核心架构解析",
+// section 1.2, among them -- are split over several waves whose partial
+// softmax statistics a second kernel merges.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -38,26 +40,42 @@ static pkv_status device_fail(int err, const char *where)
     return PKV_ERR_DEVICE;
 }
 
-static int32_t resolve_partition(const pkv_decode_args *a)
+// Compute units of the current device (256, an MI355X, when there is none).
+static int device_cu_count()
 {
-    return a->partition_tokens > 0 ? a->partition_tokens : kDefaultPartitionTokens;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64 && cached[dev] > 0)
+        return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cached[dev] = cus;
+    return cus;
 }
 
-static int32_t num_partitions(const pkv_decode_args *a)
+// Waves of the persistent grid: the caller's choice or 8 per compute unit,
+// never more than the batch can have tiles (at least 1).
+static int32_t resolve_splits(const pkv_decode_args *a)
 {
-    int32_t T = resolve_partition(a);
-    int32_t P = (a->max_context_len + T - 1) / T;
-    return P < 1 ? 1 : P;
+    const int64_t tiles_per_seq = ((int64_t)a->max_context_len + kTileTokens - 1) / kTileTokens;
+    const int64_t upper = std::max<int64_t>(1, (int64_t)a->batch * a->num_kv_heads * tiles_per_seq);
+    const int64_t want = a->num_splits > 0 ? a->num_splits : (int64_t)kDefaultWavesPerCU * device_cu_count();
+    return (int32_t)std::min<int64_t>(std::min<int64_t>(want, upper), 1 << 24);
 }
 
+// Workspace: one piece slot per (segment + wave), G query heads each.
 static size_t workspace_bytes(const pkv_decode_args *a)
 {
-    int32_t P = num_partitions(a);
-    if (P <= 1 || a->batch == 0)
+    if (a->batch == 0)
         return 0;
-    size_t units = (size_t)a->batch * (size_t)a->num_q_heads * (size_t)P;
-    size_t o = units * (size_t)a->head_dim * sizeof(float);
-    size_t ml = units * 2 * sizeof(float);
+    const size_t G = (size_t)(a->num_q_heads / a->num_kv_heads);
+    const size_t pieces = ((size_t)a->batch * (size_t)a->num_kv_heads + (size_t)resolve_splits(a)) * G;
+    const size_t o = pieces * (size_t)a->head_dim * sizeof(float);
+    const size_t ml = pieces * 2 * sizeof(float);
     return ((o + 255) & ~(size_t)255) + ml;
 }
 
@@ -74,8 +92,8 @@ static pkv_status validate(const pkv_decode_args *a)
         return fail(PKV_ERR_INVALID_ARG, "decode: num_kv_heads must divide num_q_heads");
     if ((int64_t)a->max_context_len > (int64_t)a->max_blocks * a->page_size)
         return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len exceeds max_blocks * page_size");
-    if (a->partition_tokens < 0 || a->partition_tokens % kTileTokens)
-        return fail(PKV_ERR_INVALID_ARG, "decode: partition_tokens must be 0 or a positive multiple of 64");
+    if (a->num_splits < 0)
+        return fail(PKV_ERR_INVALID_ARG, "decode: num_splits must be >= 0");
     bool kv_ok = (a->kv_dtype == PKV_I8 && (a->q_dtype == PKV_F16 || a->q_dtype == PKV_BF16)) ||
                  (a->kv_dtype == PKV_F16 && a->q_dtype == PKV_F16) ||
                  (a->kv_dtype == PKV_BF16 && a->q_dtype == PKV_BF16);
@@ -95,7 +113,7 @@ static pkv_status validate(const pkv_decode_args *a)
         ((uintptr_t)a->block_tables & 3u) || ((uintptr_t)a->context_lens & 3u))
         return fail(PKV_ERR_INVALID_ARG, "decode: q, pools and out must be 16-byte aligned, "
                                          "scales and int32 arrays 4-byte aligned");
-    size_t need = workspace_bytes(a);
+    const size_t need = workspace_bytes(a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need || ((uintptr_t)a->workspace & 255u)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace missing, smaller than "
                                        "pkv_decode_workspace_bytes, or not 256-byte aligned");
@@ -119,13 +137,13 @@ static DecodeParams make_params(const pkv_decode_args *a)
     p.num_pages = a->num_pages;
     p.max_blocks = a->max_blocks;
     p.max_context_len = a->max_context_len;
-    p.partition_tokens = resolve_partition(a);
-    p.num_partitions = num_partitions(a);
+    p.num_splits = resolve_splits(a);
     // log2(e) folded into the scale once, in fp32, so the kernels use exp2
     p.scale_log2 = a->scale * 1.44269504088896340736f;
-    if (workspace_bytes(a) > 0) {
-        size_t units = (size_t)a->batch * (size_t)a->num_q_heads * (size_t)p.num_partitions;
-        size_t o = units * (size_t)a->head_dim * sizeof(float);
+    if (a->workspace) {
+        const size_t G = (size_t)(a->num_q_heads / a->num_kv_heads);
+        const size_t pieces = ((size_t)a->batch * (size_t)a->num_kv_heads + (size_t)p.num_splits) * G;
+        const size_t o = pieces * (size_t)a->head_dim * sizeof(float);
         p.part_o = (float *)a->workspace;
         p.part_ml = (float *)((char *)a->workspace + ((o + 255) & ~(size_t)255));
     }
@@ -168,16 +186,18 @@ extern "C" pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *a, size_
     clear_error();
     if (!a || !bytes)
         return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: null argument");
-    if (a->batch < 0 || a->num_q_heads <= 0 || a->max_context_len < 0 || a->partition_tokens < 0 ||
-        a->partition_tokens % kTileTokens || a->head_dim <= 0)
+    if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->num_q_heads % a->num_kv_heads ||
+        a->max_context_len < 0 || a->num_splits < 0 || a->head_dim <= 0)
         return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: bad sizes");
     *bytes = workspace_bytes(a);
     return PKV_OK;
 }
 
-extern "C" int32_t pkv_decode_partition_tokens(const pkv_decode_args *a)
+extern "C" int32_t pkv_decode_num_splits(const pkv_decode_args *a)
 {
-    return a ? resolve_partition(a) : 0;
+    if (!a || a->batch < 0 || a->num_kv_heads <= 0 || a->max_context_len < 0 || a->num_splits < 0)
+        return 0;
+    return resolve_splits(a);
 }
 
 extern "C" pkv_status pkv_decode_validate(const pkv_decode_args *a)
@@ -205,8 +225,6 @@ extern "C" pkv_status pkv_splitk_reduce(const pkv_decode_args *a, void *stream)
     if (st != PKV_OK || a->batch == 0)
         return st;
     DecodeParams p = make_params(a);
-    if (p.num_partitions <= 1)
-        return PKV_OK;
     int err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
     return err ? device_fail(err, "pkv_splitk_reduce") : PKV_OK;
 }
@@ -222,11 +240,9 @@ extern "C" pkv_status pkv_paged_attn_decode(const pkv_decode_args *a, void *stre
                                        a->q_dtype, a->kv_dtype, stream);
     if (err)
         return device_fail(err, "pkv_paged_attn_decode (partition kernel)");
-    if (p.num_partitions > 1) {
-        err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
-        if (err)
-            return device_fail(err, "pkv_paged_attn_decode (reduce kernel)");
-    }
+    err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
+    if (err)
+        return device_fail(err, "pkv_paged_attn_decode (merge kernel)");
     return PKV_OK;
 }
 

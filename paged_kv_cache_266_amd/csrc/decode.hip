@@ -10,39 +10,47 @@
 // kernel (one thread per query, whole score matrix in shared memory) is not
 // followed.
 //
-// Design (one workgroup = one sequence b, one KV head g, one partition of
-// partition_tokens tokens; 4 waves, each wave taking every 4th 64-token tile):
+// Design.  The batch's work is the flat list of 64-token tiles of all
+// (sequence, KV head) segments; a persistent grid of single-wave workgroups
+// splits it into equal contiguous shares, whatever the length mix, so every
+// wave streams the same number of tiles (the split-K of long contexts and the
+// load balance of ragged batches are one mechanism).  Per wave:
 //
 //  * Loads.  A (page, KV head) tile is one contiguous run of page_size rows.
 //    Each lane loads 16 bytes per instruction through a buffer descriptor
 //    whose base is the page and whose size is the tile, so one instruction
 //    reads 1 KiB of consecutive rows (R = row_bytes/16 lanes per token row,
-//    64/R tokens per instruction).  Slots past the context length get an
-//    out-of-range offset and read as zero without touching memory: no
-//    garbage (or NaN) from a partly filled last page ever enters a product.
-//    K and V of a tile (R instructions each) are issued together, so a wave
-//    has 2 x 64 x R x 16 bytes in flight.
+//    64/R tokens per instruction), non-temporal.  Slots past the context
+//    length get an out-of-range offset and read as zero without touching
+//    memory: no garbage (or NaN) from a partly filled last page ever enters a
+//    product.
+//  * Pipelining.  One ring of R 16-byte registers per lane holds K of tile t,
+//    then V of tile t, then K of tile t+1: each chunk's V load is issued as
+//    soon as its K has been used and the next tile's K as soon as its V has
+//    been used, so a tile of K/V is always in flight behind the arithmetic,
+//    across segment boundaries too (the next segment's q is fetched a tile
+//    ahead).
 //  * q.k.  Lane (row r, column j) holds 16 bytes of one token row and the
 //    matching slice of each of the G query heads of the group; dot2
 //    instructions (f16/bf16) or byte conversions + FMAs (int8) give partial
-//    dots.  A DPP reduce-scatter over the R lanes of a row leaves each lane
-//    with the full scores of ONE token (token r + (64/R) j of the tile) for
-//    all G heads -- no redundant softmax work.
+//    dots, folded into a DPP reduce-scatter tree over the R lanes of a row
+//    chunk by chunk.  Each lane ends with the full scores of ONE token (token
+//    r + (64/R) j of the tile) for all G heads -- no redundant softmax work.
 //  * Online softmax.  Tile max per head by DPP row rotations and a
 //    wave-uniform combine of the four rows; running max, per-lane running
-//    sums, exp2 with
-//    log2(e) folded into the scale.  For int8, the V scale of the token is
-//    folded into its probability and the K scale into its score.
+//    sums, exp2 with log2(e) folded into the scale.  For int8, the V scale of
+//    the token is folded into its probability and the K scale into its score.
 //  * p.V.  Probabilities go to a per-wave LDS slot; each lane then reads, per
 //    chunk, the G probabilities of the token whose V bytes it holds
 //    (broadcast reads) and accumulates G x (elements per lane) fp32 sums.
-//  * Combine.  Rows, then waves (through LDS), then -- when the sequence
-//    spans several partitions -- the split-K reduce kernel merges
-//    (max, sum, unnormalised output) partials.
+//  * Combine.  Token rows are summed across lanes.  A segment a wave covers
+//    whole is written directly; the pieces of a segment shared by waves go to
+//    the workspace as (max, sum, unnormalised output) for the merge kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <utility>
 
 #include "internal.h"
 
@@ -53,6 +61,15 @@ typedef uint32_t u32;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Cache policy of the K/V loads: non-temporal.  Every K/V byte is read once
+// per step, so keeping it out of the caches' normal replacement raises the
+// sustained read rate (measured on gfx950: ~6.8 vs ~6.05 TB/s for a pure
+// page-tile stream).
+#ifndef PKV_KV_CPOL
+#define PKV_KV_CPOL 2
+#endif
+constexpr int kStreamingLoad = PKV_KV_CPOL;
 
 constexpr u32 kBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;    // voffset that fails the range check
@@ -66,19 +83,11 @@ __device__ __forceinline__ float dpp(float x)
                                                                  0xF, 0xF, false));
 }
 
-// DPP controls: partner lane for the reduce-scatter bit, and row rotations.
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141; // j <-> 7-j within each 8 lanes
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;       // j <-> j^8 within each 16 lanes
-
-template <int BIT>
-struct Partner;
-template <> struct Partner<0> { static constexpr int ctrl = kQuadXor1; };
-template <> struct Partner<1> { static constexpr int ctrl = kQuadXor2; };
-template <> struct Partner<2> { static constexpr int ctrl = kRowHalfMirror; };
-template <> struct Partner<3> { static constexpr int ctrl = kRowRor8; };
+// DPP controls (lane j of a 16-lane row reads lane ...):
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]: j ^ 1
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]: j ^ 2
+constexpr int kRowRor4 = 0x124;       // row_ror 4: j - 4 (mod 16)
+constexpr int kRowRor8 = 0x128;       // row_ror 8: j ^ 8
 
 // Full reductions over the 64 lanes.  DPP rotations finish each 16-lane row;
 // the four row results are then read as wave-uniform values.
@@ -119,42 +128,49 @@ __device__ __forceinline__ float sum_over_rows(float x)
     return x;
 }
 
-// One reduce-scatter step over lanes that differ in bit BIT of the column:
-// lanes with that bit clear keep (and complete) the lower half of the
-// values, lanes with it set the upper half.
-template <int N, int BIT>
-__device__ __forceinline__ void rs_step(const float (&in)[N], float (&out)[N / 2], bool upper)
+// Reduce-scatter of per-chunk partial dots over the R lanes of a token row,
+// built as a binary tree from the lowest column bit up so that chunks can be
+// folded in as soon as they are computed.  At level b, lanes whose column has
+// bit b clear keep the lower of two values (chunk range with that bit 0) and
+// add their partner's copy of it; lanes with the bit set keep the upper one.
+// After log2(R) levels, column j holds the full dot of chunk j.
+//
+// Partner lane at level b is j ^ 2^b: quad permutations for b < 2; for b = 2
+// the lower lane reads j + 4 (row_ror 12) and the upper lane j - 4
+// (row_ror 4); for b = 3, row_ror 8.
+template <int B>
+struct Level;
+template <> struct Level<0> { static constexpr int lo = kQuadXor1, up = kQuadXor1; };
+template <> struct Level<1> { static constexpr int lo = kQuadXor2, up = kQuadXor2; };
+template <> struct Level<2> { static constexpr int lo = 0x12C, up = kRowRor4; };
+template <> struct Level<3> { static constexpr int lo = kRowRor8, up = kRowRor8; };
+
+template <int B, int G>
+__device__ __forceinline__ void tree_combine(float (&lo)[G], const float (&up)[G], int j)
 {
+    const bool upper = (j >> B) & 1;
 #pragma unroll
-    for (int x = 0; x < N / 2; ++x) {
-        const float lo = in[x], up = in[x + N / 2];
-        const float a = lo + dpp<Partner<BIT>::ctrl>(lo);
-        const float c = up + dpp<Partner<BIT>::ctrl>(up);
-        out[x] = upper ? c : a;
+    for (int h = 0; h < G; ++h) {
+        const float a = lo[h] + dpp<Level<B>::lo>(lo[h]);
+        const float c = up[h] + dpp<Level<B>::up>(up[h]);
+        lo[h] = upper ? c : a;
     }
 }
 
-// in[i * G + h] = partial of chunk i, head h on column j of an R-lane row;
-// out[h] = full value of chunk j, head h.
-template <int R, int G>
-__device__ __forceinline__ void reduce_scatter(const float (&in)[R * G], float (&out)[G], int j)
+// Fold chunk I's partials v into the pending-value stack (binary counter on I).
+template <int I, int B, int LEVELS, int G>
+__device__ __forceinline__ void tree_push(float (&stack)[LEVELS + 1][G], float (&v)[G], int j)
 {
-    if constexpr (R == 16) {
-        float t8[8 * G], t4[4 * G], t2[2 * G];
-        rs_step<16 * G, 3>(in, t8, (j & 8) != 0);
-        rs_step<8 * G, 2>(t8, t4, (j & 4) != 0);
-        rs_step<4 * G, 1>(t4, t2, (j & 2) != 0);
-        rs_step<2 * G, 0>(t2, out, (j & 1) != 0);
-    } else if constexpr (R == 8) {
-        float t4[4 * G], t2[2 * G];
-        rs_step<8 * G, 2>(in, t4, (j & 4) != 0);
-        rs_step<4 * G, 1>(t4, t2, (j & 2) != 0);
-        rs_step<2 * G, 0>(t2, out, (j & 1) != 0);
+    if constexpr (B < LEVELS && ((I >> B) & 1)) {
+        tree_combine<B, G>(stack[B], v, j);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            v[h] = stack[B][h];
+        tree_push<I, B + 1, LEVELS, G>(stack, v, j);
     } else {
-        static_assert(R == 4, "row split");
-        float t2[2 * G];
-        rs_step<4 * G, 1>(in, t2, (j & 2) != 0);
-        rs_step<2 * G, 0>(t2, out, (j & 1) != 0);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            stack[B][h] = v[h];
     }
 }
 
@@ -212,205 +228,367 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, in
 
 template <int D, int PS, int G, int QT, int KVT>
 struct Shape {
+    static constexpr int PAGE = PS;                // tokens per page
     static constexpr int EB = KVT == I8 ? 1 : 2;   // bytes per KV element
     static constexpr int ROW = D * EB;             // bytes per token row
     static constexpr int R = ROW / 16;             // lanes per token row
+    static constexpr int LEVELS = R == 16 ? 4 : R == 8 ? 3 : 2;
     static constexpr int TPI = 64 / R;             // tokens per load instruction
     static constexpr int EPL = 16 / EB;            // elements per lane chunk
     static constexpr int TILE_BYTES = PS * ROW;    // one (page, KV head) tile
-    static constexpr int PAGES_PER_TILE = kTileTokens / PS;
-    static constexpr int PSTRIDE = 64 * G + (64 / R) * 4;  // floats per wave in the p buffer
+    static constexpr int PPT = kTileTokens / PS;   // pages per 64-token tile
+    static constexpr int PSTRIDE = 64 * G + (64 / R) * 4;  // floats in the p buffer
     static_assert(R >= 4 && R <= 16, "row split");
     static_assert(PS % TPI == 0, "a load instruction must not straddle pages");
     static_assert(kTileTokens % PS == 0, "tiles hold whole pages");
 };
 
-template <int D, int PS, int G, int QT, int KVT>
-__global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeParams p)
-{
-    using S = Shape<D, PS, G, QT, KVT>;
-    constexpr int R = S::R, TPI = S::TPI, EPL = S::EPL;
-    constexpr bool kI8 = KVT == I8;
+// Where the 16 bytes of chunk i of a 64-token tile come from, for this lane.
+// base[] is the (page, KV head) tile of each page of the tile (page 0 stands
+// in for a page that does not exist; nothing is read from it).  The lane's
+// byte offset within a page is the same for every chunk; the chunk's own
+// offset within the page is a compile-time scalar.  A lane whose token of
+// chunk i is at or past the end of the tile (chunk index >= nvalid) gets an
+// out-of-range offset and reads zero without touching memory, so loads are
+// issued unconditionally, also for a tile that is not there (nvalid = 0).
+template <class S>
+struct TileAddr {
+    const char *base[S::PPT];
+    int nvalid;   // chunks of this tile that hold a token for this lane's row
 
-    __shared__ float s_p[kWaves * S::PSTRIDE];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    __shared__ float s_o[kWaves][G][D];
-
-    const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int T = p.partition_tokens;
-    const int Hq = p.num_q_heads;
-    const int hq0 = g * G;
-
-    int n = p.context_lens[b];
-    bool bad = n < 0 || n > p.max_context_len;
-    if (bad)
-        n = 0;
-    const int t_begin = part * T;
-    if (part > 0 && t_begin >= n)
-        return;                              // partition past the end (uniform)
-    const bool single = n <= T;              // this workgroup owns the whole sequence
-
-    if (n == 0) {                            // empty (or invalid) sequence: zeros (NaN)
-        const float fill = bad ? __builtin_nanf("") : 0.0f;
-        for (int i = threadIdx.x; i < G * D / 2; i += kWaves * 64) {
-            int h = i / (D / 2), d2 = (i % (D / 2)) * 2;
-            u32 *o = reinterpret_cast<u32 *>(p.out) + (((size_t)b * Hq + hq0 + h) * D + d2) / 2;
-            *o = pack_out<QT>(fill, fill);
-        }
-        return;
+    __device__ __forceinline__ void set(const char *head, size_t page_stride, const int (&ph)[S::PPT],
+                                        int rem, int r)
+    {
+#pragma unroll
+        for (int pg = 0; pg < S::PPT; ++pg)
+            base[pg] = head + (size_t)(ph[pg] >= 0 ? ph[pg] : 0) * page_stride;
+        // token i*TPI + r exists iff i*TPI + r < rem
+        nvalid = rem > r ? (rem - r + S::TPI - 1) / S::TPI : 0;
     }
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int r = lane / R, j = lane % R;
-    const int t_end = min(n, t_begin + T);
-    const int n_tiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-    const int tile_base = t_begin / kTileTokens;   // T is a multiple of 64
-
-    // ---- this lane's slice of the G query heads
-    u32 qw[G][4];         // 16-bit KV: packed pairs matching the K chunk
-    float qf[kI8 ? G : 1][kI8 ? 16 : 1];
-    float qbias[G];       // int8: -128 * sum of the lane's q slice
+    template <int I>
+    __device__ __forceinline__ u32x4 load(int lane_off) const
     {
-        const char *qb = (const char *)p.q + (((size_t)b * Hq + hq0) * D) * 2;
+        constexpr int pg = (I * S::TPI) / S::PAGE;
+        constexpr int chunk_off = ((I * S::TPI) % S::PAGE) * S::ROW;
+        const int voff = I < nvalid ? lane_off : kOutOfRange;
+        return __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(base[pg], S::TILE_BYTES), voff, chunk_off, kStreamingLoad);
+    }
+};
+
+// ---- batch geometry ---------------------------------------------------------
+//
+// The work of a decode step is the flat list of 64-token tiles of every
+// (sequence b, KV head g) "segment", in the order b, then g, then tile index
+// k.  Sequence b contributes tiles_b = ceil(n_b / 64) tiles to each of its Hkv
+// segments (0 for an empty or invalid sequence), so segment s = b*Hkv + g
+// starts at global tile Hkv * sum_{b'<b} tiles_b' + g * tiles_b.  Wave w of a
+// grid of NW waves streams the global tiles [w*T/NW, (w+1)*T/NW) where T is
+// the total (waves beyond T idle, so no range is empty); a segment it covers
+// completely is finished by that wave, the pieces of a segment shared by
+// several waves are merged by the second kernel.  Piece (s, w) is stored at
+// index s + w, which is unique.
+
+__device__ __forceinline__ int tiles_of(int n, int max_len)
+{
+    return n >= 0 && n <= max_len ? (n + kTileTokens - 1) / kTileTokens : 0;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    return x;
+}
+
+// Tiles of one KV head over the whole batch.
+__device__ __forceinline__ int batch_tiles(const DecodeParams &p, int lane)
+{
+    int total = 0;
+    for (int c = 0; c < p.batch; c += 64) {
+        const int b = c + lane;
+        total += wave_sum_int(b < p.batch ? tiles_of(p.context_lens[b], p.max_context_len) : 0);
+    }
+    return total;
+}
+
+// Range of global tiles owned by wave w of NW.
+__device__ __forceinline__ long long range_start(long long w, long long T, long long NW)
+{
+    return w * T / NW;
+}
+
+// The wave that owns global tile t (largest w with range_start(w) <= t).
+__device__ __forceinline__ long long owner_of(long long t, long long T, long long NW)
+{
+    return ((t + 1) * NW - 1) / T;
+}
+
+// Sequence containing global tile t (t < total) and the first global tile of
+// that sequence: walks the batch 64 sequences at a time.
+__device__ __forceinline__ void locate(const DecodeParams &p, long long t, int lane, int &b_out,
+                                       long long &start_out)
+{
+    int carry = 0;
+    const int Hkv = p.num_kv_heads;
+    for (int c = 0; c < p.batch; c += 64) {
+        const int b = c + lane;
+        const int nt = b < p.batch ? tiles_of(p.context_lens[b], p.max_context_len) : 0;
+        const int incl = wave_incl_scan(nt, lane);
+        const bool past = b < p.batch && (long long)(carry + incl) * Hkv > t;
+        const unsigned long long mask = __ballot(past);
+        if (mask) {
+            const int first = __builtin_ctzll(mask);
+            b_out = c + first;
+            start_out = (long long)(carry + __shfl(incl - nt, first)) * Hkv;
+            return;
+        }
+        carry += __shfl(incl, 63);
+    }
+    b_out = p.batch;
+    start_out = 0;
+}
+
+// ---- the partition kernel ---------------------------------------------------
+
+template <int D, int PS, int G, int QT, int KVT>
+__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
+{
+    using S = Shape<D, PS, G, QT, KVT>;
+    constexpr int R = S::R, TPI = S::TPI, EPL = S::EPL, PPT = S::PPT, LEVELS = S::LEVELS;
+    constexpr bool kI8 = KVT == I8;
+    constexpr int QW = kI8 ? 8 : 4;   // dwords of q per head per lane
+
+    __shared__ float s_p[S::PSTRIDE];
+
+    const int lane = threadIdx.x;
+    const int r = lane / R, j = lane % R;
+    const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+    const long long NW = gridDim.x, w = blockIdx.x;
+
+    const long long T = (long long)batch_tiles(p, lane) * Hkv;
+    // waves beyond the tile count idle, so every working wave's range is non-empty
+    const long long NWe = NW < T ? NW : T;
+    if (w >= NWe)
+        return;
+    const long long lo = range_start(w, T, NWe), hi = range_start(w + 1, T, NWe);
+
+    // ---- the tile cursor: sequence b (length n, tiles nt), KV head g, tile k
+    struct Cursor {
+        int b, n, nt, g, k;
+    };
+    Cursor cur;
+    {
+        long long start;
+        locate(p, lo, lane, cur.b, start);
+        cur.n = p.context_lens[cur.b];
+        cur.nt = tiles_of(cur.n, p.max_context_len);
+        const long long off = lo - start;
+        cur.g = (int)(off / cur.nt);
+        cur.k = (int)(off % cur.nt);
+    }
+    auto advance = [&](const Cursor &c) {
+        Cursor x = c;
+        if (++x.k == x.nt) {
+            x.k = 0;
+            if (++x.g == Hkv) {
+                x.g = 0;
+                // next sequence with at least one tile (one exists: this wave
+                // only advances while tiles of its range remain)
+                do {
+                    ++x.b;
+                    x.n = x.b < p.batch ? p.context_lens[x.b] : 0;
+                    x.nt = tiles_of(x.n, p.max_context_len);
+                } while (x.nt == 0 && x.b < p.batch);
+            }
+        }
+        return x;
+    };
+
+    bool any_bad = false;
+    const size_t page_stride = (size_t)Hkv * S::TILE_BYTES;
+    // Physical pages of the cursor's tile (-1: none / outside the pool); the
+    // table is read at a clamped index so the lookup needs no branch.
+    auto pages_of = [&](const Cursor &c, int (&ph)[PPT]) {
+        const int32_t *bt = p.block_tables + (size_t)min(c.b, p.batch - 1) * p.max_blocks;
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg) {
+            const int v = bt[min(c.k * PPT + pg, p.max_blocks - 1)];
+            const bool exists = c.k * kTileTokens + pg * PS < c.n;
+            const bool inside = (unsigned)v < (unsigned)p.num_pages;
+            any_bad = any_bad || (exists && !inside);
+            ph[pg] = exists && inside ? v : -1;
+        }
+    };
+    auto tile_rem = [&](const Cursor &c) { return min(kTileTokens, c.n - c.k * kTileTokens); };
+    auto own_page = [&](const int (&ph)[PPT]) {
+        int my_phys = -1;
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg)
+            if (pg == (TPI * j) / PS)
+                my_phys = ph[pg];
+        return my_phys;
+    };
+    // K and V scales of this lane's own token of the cursor's tile (int8).
+    auto own_scales = [&](const Cursor &c, const int (&ph)[PPT], float &ks, float &vs) {
+        ks = 1.0f;
+        vs = 1.0f;
+        if constexpr (kI8) {
+            const int my_phys = own_page(ph);
+            const bool ok = my_phys >= 0 && c.k * kTileTokens + TPI * j + r < c.n;
+            const size_t si = ok ? ((size_t)my_phys * Hkv + c.g) * PS + (TPI * j) % PS + r : 0;
+            const float a = p.k_scale[si], b = p.v_scale[si];
+            ks = ok ? a : 0.0f;
+            vs = ok ? b : 0.0f;
+        }
+    };
+    // Raw q dwords of this lane's slice of the G query heads of segment (b, g).
+    auto load_q = [&](const Cursor &c, u32 (&raw)[G][QW]) {
+        const char *base = (const char *)p.q + (((size_t)c.b * Hq + (size_t)c.g * G) * D) * 2;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(base + ((size_t)h * D + EPL * j) * 2);
+#pragma unroll
+            for (int v = 0; v < QW / 4; ++v) {
+                const u32x4 x = src[v];
+                raw[h][4 * v] = x.x;
+                raw[h][4 * v + 1] = x.y;
+                raw[h][4 * v + 2] = x.z;
+                raw[h][4 * v + 3] = x.w;
+            }
+        }
+    };
+
+    // q in the form the dot products use: packed pairs (16-bit KV) or fp32
+    // values with the -128 * sum(q) bias of the unsigned-byte trick (int8).
+    u32 qw[G][4];
+    float qf[kI8 ? G : 1][kI8 ? 16 : 1];
+    float qbias[G];
+    auto set_q = [&](const u32 (&raw)[G][QW]) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if constexpr (!kI8) {
-                u32x4 v = *reinterpret_cast<const u32x4 *>(qb + ((size_t)h * D + EPL * j) * 2);
-                qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    qw[h][v] = raw[h][v];
                 qbias[h] = 0.0f;
             } else {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(qb + ((size_t)h * D + 16 * j) * 2);
-                u32x4 a = src[0], c = src[1];
-                u32 w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
                 float s = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    qf[h][2 * e] = q_lo<QT>(w[e]);
-                    qf[h][2 * e + 1] = q_hi<QT>(w[e]);
+                    qf[h][2 * e] = q_lo<QT>(raw[h][e]);
+                    qf[h][2 * e + 1] = q_hi<QT>(raw[h][e]);
                     s += qf[h][2 * e] + qf[h][2 * e + 1];
                 }
                 qbias[h] = -128.0f * s;
             }
         }
-    }
+    };
 
     float m_run[G], l_run[G], acc[G][EPL], psum[G];
+    auto reset_state = [&]() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m_run[h] = -INFINITY;
-        l_run[h] = 0.0f;
-        psum[h] = 0.0f;
+        for (int h = 0; h < G; ++h) {
+            m_run[h] = -INFINITY;
+            l_run[h] = 0.0f;
+            psum[h] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            acc[h][e] = 0.0f;
-    }
-
-    const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
-    const size_t page_stride = (size_t)p.num_kv_heads * S::TILE_BYTES;
-    const char *k_head = (const char *)p.k_pool + (size_t)g * S::TILE_BYTES;
-    const char *v_head = (const char *)p.v_pool + (size_t)g * S::TILE_BYTES;
-    float *pbuf = s_p + wave * S::PSTRIDE;
-    bool wave_bad = false;
-
-    for (int tile = wave; tile < n_tiles; tile += kWaves) {
-        const int tg = tile_base + tile;       // global tile index
-        const int t0 = tg * kTileTokens;       // first token of the tile
-
-        // ---- issue K and V loads of the whole tile
-        u32x4 kr[R], vr[R];
-        int phys_of_page[S::PAGES_PER_TILE];
-#pragma unroll
-        for (int pg = 0; pg < S::PAGES_PER_TILE; ++pg) {
-            const int tp = t0 + pg * PS;
-            int phys = -1;
-            if (tp < t_end) {
-                phys = bt[tg * S::PAGES_PER_TILE + pg];
-                if ((unsigned)phys >= (unsigned)p.num_pages) {
-                    wave_bad = true;
-                    phys = -1;
-                }
-            }
-            phys_of_page[pg] = phys;
+            for (int e = 0; e < EPL; ++e)
+                acc[h][e] = 0.0f;
         }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int pg = (i * TPI) / PS;
-            const int phys = phys_of_page[pg];
-            const int tok = t0 + i * TPI + r;
-            const bool valid = phys >= 0 && tok < t_end;
-            const int voff = valid ? (((i * TPI) % PS + r) * S::ROW + 16 * j) : kOutOfRange;
-            const size_t poff = (size_t)(phys < 0 ? 0 : phys) * page_stride;
-            kr[i] = load16(tile_rsrc(k_head + poff, S::TILE_BYTES), voff);
-            vr[i] = load16(tile_rsrc(v_head + poff, S::TILE_BYTES), voff);
-        }
+    };
 
-        // this lane's token after the reduce-scatter: r + TPI * j
-        const int my_tok = t0 + TPI * j + r;
-        const int my_pg = (TPI * j) / PS;
-        int my_phys = -1;
-#pragma unroll
-        for (int pg = 0; pg < S::PAGES_PER_TILE; ++pg)
-            if (pg == my_pg)
-                my_phys = phys_of_page[pg];
-        const bool my_valid = my_phys >= 0 && my_tok < t_end;
-        float kscale = 1.0f, vscale = 1.0f;
-        if constexpr (kI8) {
-            if (my_valid) {
-                size_t si = ((size_t)my_phys * p.num_kv_heads + g) * PS + (TPI * j) % PS + r;
-                kscale = p.k_scale[si];
-                vscale = p.v_scale[si];
-            }
-        }
+    // ---- prologue.  One register ring of R chunks carries, in turn, K of
+    // tile t, V of tile t, K of tile t+1, ...: each chunk's V load is issued
+    // as soon as its K has been used, and the next tile's K as soon as its V
+    // has been used -- across segment boundaries too.
+    const int lane_off = r * S::ROW + 16 * j;
+    int ph_cur[PPT], ph_nxt[PPT];
+    pages_of(cur, ph_cur);
+    TileAddr<S> ka, va;
+    ka.set((const char *)p.k_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
+    va.set((const char *)p.v_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
+    u32x4 ring[R];
+    [&]<int... I>(std::integer_sequence<int, I...>) { ((ring[I] = ka.template load<I>(lane_off)), ...); }
+        (std::make_integer_sequence<int, R>{});
+    u32 qraw[G][QW];
+    load_q(cur, qraw);
+    set_q(qraw);
+    reset_state();
+    float ks_cur, vs_cur, ks_nxt = 1.0f, vs_nxt = 1.0f;
+    own_scales(cur, ph_cur, ks_cur, vs_cur);
+    bool piece_from_start = cur.k == 0;
 
-        // ---- partial dots: part[i][h] over this lane's 16 bytes of chunk i
-        float part_[R * G];
+    for (long long t = lo; t < hi; ++t) {
+        const bool last_in_range = t + 1 == hi;
+        const Cursor nxt = last_in_range ? cur : advance(cur);
+        const bool seg_end = last_in_range || nxt.k == 0;
+        if (!last_in_range)
+            pages_of(nxt, ph_nxt);
+        else
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
+            for (int pg = 0; pg < PPT; ++pg)
+                ph_nxt[pg] = -1;
+        // next segment's q goes out now; it is used after this tile
+        if (seg_end && !last_in_range)
+            load_q(nxt, qraw);
+
+        // ---- q.k: partial dots of chunk i, folded into the reduce-scatter
+        // tree as they come; chunk i's registers then take V of this tile
+        float stack[LEVELS + 1][G];
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (([&] {
+                 float v[G];
+                 const u32x4 kc = ring[I];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float a;
-                if constexpr (!kI8) {
-                    a = dot2<KVT>(kr[i].x, qw[h][0], 0.0f);
-                    a = dot2<KVT>(kr[i].y, qw[h][1], a);
-                    a = dot2<KVT>(kr[i].z, qw[h][2], a);
-                    a = dot2<KVT>(kr[i].w, qw[h][3], a);
-                } else {
-                    // code + 128 as unsigned bytes; the -128 * sum(q) bias restores the sign
-                    const u32 w0 = kr[i].x ^ 0x80808080u, w1 = kr[i].y ^ 0x80808080u;
-                    const u32 w2 = kr[i].z ^ 0x80808080u, w3 = kr[i].w ^ 0x80808080u;
-                    a = qbias[h];
-                    a = fmaf(qf[h][0], ubyte<0>(w0), a);
-                    a = fmaf(qf[h][1], ubyte<1>(w0), a);
-                    a = fmaf(qf[h][2], ubyte<2>(w0), a);
-                    a = fmaf(qf[h][3], ubyte<3>(w0), a);
-                    a = fmaf(qf[h][4], ubyte<0>(w1), a);
-                    a = fmaf(qf[h][5], ubyte<1>(w1), a);
-                    a = fmaf(qf[h][6], ubyte<2>(w1), a);
-                    a = fmaf(qf[h][7], ubyte<3>(w1), a);
-                    a = fmaf(qf[h][8], ubyte<0>(w2), a);
-                    a = fmaf(qf[h][9], ubyte<1>(w2), a);
-                    a = fmaf(qf[h][10], ubyte<2>(w2), a);
-                    a = fmaf(qf[h][11], ubyte<3>(w2), a);
-                    a = fmaf(qf[h][12], ubyte<0>(w3), a);
-                    a = fmaf(qf[h][13], ubyte<1>(w3), a);
-                    a = fmaf(qf[h][14], ubyte<2>(w3), a);
-                    a = fmaf(qf[h][15], ubyte<3>(w3), a);
-                }
-                part_[i * G + h] = a;
-            }
-        }
+                 for (int h = 0; h < G; ++h) {
+                     float a;
+                     if constexpr (!kI8) {
+                         a = dot2<KVT>(kc.x, qw[h][0], 0.0f);
+                         a = dot2<KVT>(kc.y, qw[h][1], a);
+                         a = dot2<KVT>(kc.z, qw[h][2], a);
+                         a = dot2<KVT>(kc.w, qw[h][3], a);
+                     } else {
+                         // code + 128 as unsigned bytes; the -128 * sum(q) bias restores the sign
+                         const u32 wd[4] = {kc.x ^ 0x80808080u, kc.y ^ 0x80808080u, kc.z ^ 0x80808080u,
+                                            kc.w ^ 0x80808080u};
+                         a = qbias[h];
+#pragma unroll
+                         for (int q4 = 0; q4 < 4; ++q4) {
+                             a = fmaf(qf[h][4 * q4 + 0], ubyte<0>(wd[q4]), a);
+                             a = fmaf(qf[h][4 * q4 + 1], ubyte<1>(wd[q4]), a);
+                             a = fmaf(qf[h][4 * q4 + 2], ubyte<2>(wd[q4]), a);
+                             a = fmaf(qf[h][4 * q4 + 3], ubyte<3>(wd[q4]), a);
+                         }
+                     }
+                     v[h] = a;
+                 }
+                 ring[I] = va.template load<I>(lane_off);
+                 tree_push<I, 0, LEVELS, G>(stack, v, j);
+             }()), ...);
+        }(std::make_integer_sequence<int, R>{});
 
-        // ---- reduce-scatter over the R lanes of a row: lane j keeps chunk j
-        float sc[G];
-        reduce_scatter<R, G>(part_, sc, j);
-
-        // ---- online softmax (log2 domain)
+        // ---- online softmax (log2 domain); this lane's token is TPI*j + r
+        const int t0 = cur.k * kTileTokens;
+        const int my_phys = own_page(ph_cur);
+        const bool my_valid = my_phys >= 0 && t0 + TPI * j + r < cur.n;
+        own_scales(nxt, ph_nxt, ks_nxt, vs_nxt);
         float pe[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float s = my_valid ? sc[h] * kscale * p.scale_log2 : -INFINITY;
+            const float s = my_valid ? stack[LEVELS][h] * ks_cur * p.scale_log2 : -INFINITY;
             const float m_new = fmaxf(m_run[h], wave_max(s));
             const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
             const float e = __builtin_amdgcn_exp2f(s - m_new);
@@ -420,11 +598,11 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeParams 
 #pragma unroll
             for (int x = 0; x < EPL; ++x)
                 acc[h][x] *= alpha;
-            pe[h] = e * vscale;
+            pe[h] = e * vs_cur;
         }
 
         // ---- hand each probability to the lanes holding that token's V bytes
-        float *mine = pbuf + lane * G + r * 4;
+        float *mine = s_p + lane * G + r * 4;
 #pragma unroll
         for (int h = 0; h < G; ++h)
             mine[h] = pe[h];
@@ -432,132 +610,170 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_kernel(DecodeParams 
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        // the next tile's K goes into each chunk's registers once its V is used
+        ka.set((const char *)p.k_pool + (size_t)nxt.g * S::TILE_BYTES, page_stride, ph_nxt,
+               last_in_range ? 0 : tile_rem(nxt), r);
+
+        // ---- p.V
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (([&] {
+                 const float *src = s_p + (r * R + I) * G + r * 4;
+                 float pv[G];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float *src = pbuf + (r * R + i) * G + r * 4;
-            float pv[G];
+                 for (int h = 0; h < G; ++h)
+                     pv[h] = src[h];
+                 const u32x4 vc = ring[I];
+                 ring[I] = ka.template load<I>(lane_off);
+                 float vf[EPL];
+                 const u32 wv[4] = {vc.x, vc.y, vc.z, vc.w};
+                 if constexpr (kI8) {
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-                pv[h] = src[h];
-            float vf[EPL];
-            const u32 w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-            if constexpr (kI8) {
+                     for (int q4 = 0; q4 < 4; ++q4) {
+                         const u32 u = wv[q4] ^ 0x80808080u;
+                         vf[4 * q4 + 0] = ubyte<0>(u);
+                         vf[4 * q4 + 1] = ubyte<1>(u);
+                         vf[4 * q4 + 2] = ubyte<2>(u);
+                         vf[4 * q4 + 3] = ubyte<3>(u);
+                     }
+                 } else {
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const u32 u = w[q4] ^ 0x80808080u;
-                    vf[4 * q4 + 0] = ubyte<0>(u);
-                    vf[4 * q4 + 1] = ubyte<1>(u);
-                    vf[4 * q4 + 2] = ubyte<2>(u);
-                    vf[4 * q4 + 3] = ubyte<3>(u);
-                }
-            } else {
+                     for (int q2 = 0; q2 < 4; ++q2) {
+                         vf[2 * q2] = KVT == BF16 ? bf16_lo(wv[q2]) : f16_lo(wv[q2]);
+                         vf[2 * q2 + 1] = KVT == BF16 ? bf16_hi(wv[q2]) : f16_hi(wv[q2]);
+                     }
+                 }
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    vf[2 * q2] = KVT == BF16 ? bf16_lo(w[q2]) : f16_lo(w[q2]);
-                    vf[2 * q2 + 1] = KVT == BF16 ? bf16_hi(w[q2]) : f16_hi(w[q2]);
-                }
-            }
+                 for (int h = 0; h < G; ++h) {
+                     if constexpr (kI8)
+                         psum[h] += pv[h];
+#pragma unroll
+                     for (int x = 0; x < EPL; ++x)
+                         acc[h][x] = fmaf(pv[h], vf[x], acc[h][x]);
+                 }
+             }()), ...);
+        }(std::make_integer_sequence<int, R>{});
+        __builtin_amdgcn_wave_barrier();
+        va.set((const char *)p.v_pool + (size_t)nxt.g * S::TILE_BYTES, page_stride, ph_nxt,
+               last_in_range ? 0 : tile_rem(nxt), r);
+
+        // ---- end of a piece: this wave's share of segment (cur.b, cur.g)
+        if (seg_end) {
+            const bool whole = piece_from_start && cur.k == cur.nt - 1;
+            const int seg = cur.b * Hkv + cur.g;
+            const float nan = __builtin_nanf("");
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                if constexpr (kI8)
-                    psum[h] += pv[h];
+                if constexpr (kI8) {
+#pragma unroll
+                    for (int x = 0; x < EPL; ++x)
+                        acc[h][x] = fmaf(-128.0f, psum[h], acc[h][x]);
+                }
+                const float lt = wave_sum(l_run[h]);
 #pragma unroll
                 for (int x = 0; x < EPL; ++x)
-                    acc[h][x] = fmaf(pv[h], vf[x], acc[h][x]);
+                    acc[h][x] = sum_over_rows<R>(acc[h][x]);
+                if (r == 0) {
+                    if (whole) {
+                        const size_t unit = (size_t)cur.b * Hq + (size_t)cur.g * G + h;
+                        const float inv = any_bad ? nan : 1.0f / lt;
+                        u32 packed[EPL / 2];
+#pragma unroll
+                        for (int x = 0; x < EPL / 2; ++x)
+                            packed[x] = pack_out<QT>(acc[h][2 * x] * inv, acc[h][2 * x + 1] * inv);
+                        u32x4 *o = reinterpret_cast<u32x4 *>(reinterpret_cast<u32 *>(p.out) + (unit * D + EPL * j) / 2);
+#pragma unroll
+                        for (int v = 0; v < EPL / 8; ++v)
+                            o[v] = u32x4{packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]};
+                    } else {
+                        const size_t piece = ((size_t)seg + (size_t)w) * G + h;
+                        float4 *po = reinterpret_cast<float4 *>(p.part_o + piece * D + EPL * j);
+#pragma unroll
+                        for (int v = 0; v < EPL / 4; ++v)
+                            po[v] = any_bad ? make_float4(nan, nan, nan, nan)
+                                            : make_float4(acc[h][4 * v], acc[h][4 * v + 1], acc[h][4 * v + 2],
+                                                          acc[h][4 * v + 3]);
+                        if (j == 0)
+                            *reinterpret_cast<float2 *>(p.part_ml + piece * 2) =
+                                make_float2(m_run[h], any_bad ? nan : lt);
+                    }
+                }
             }
+            reset_state();
+            any_bad = false;
+            piece_from_start = true;
+            if (!last_in_range)
+                set_q(qraw);
         }
-        __builtin_amdgcn_wave_barrier();
-    }
 
-    // ---- wave totals
+        // ---- roll the window forward
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        if constexpr (kI8) {
-#pragma unroll
-            for (int x = 0; x < EPL; ++x)
-                acc[h][x] = fmaf(-128.0f, psum[h], acc[h][x]);
-        }
-        const float lt = wave_sum(l_run[h]);
-#pragma unroll
-        for (int x = 0; x < EPL; ++x)
-            acc[h][x] = sum_over_rows<R>(acc[h][x]);
-        if (lane == 0) {
-            s_m[wave][h] = m_run[h];
-            s_l[wave][h] = lt;
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int x = 0; x < EPL; ++x)
-                s_o[wave][h][EPL * j + x] = acc[h][x];
-        }
-    }
-    // a bad page anywhere in the workgroup poisons the result
-    const bool any_bad = __syncthreads_or(wave_bad ? 1 : 0) != 0;
-
-    // ---- merge the waves; write the output or this partition's partials
-    for (int i = threadIdx.x; i < G * D / 2; i += kWaves * 64) {
-        const int h = i / (D / 2), d2 = (i % (D / 2)) * 2;
-        float M = s_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            M = fmaxf(M, s_m[w][h]);
-        float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-            L = fmaf(f, s_l[w][h], L);
-            o0 = fmaf(f, s_o[w][h][d2], o0);
-            o1 = fmaf(f, s_o[w][h][d2 + 1], o1);
-        }
-        if (any_bad) {
-            L = __builtin_nanf("");
-            o0 = o1 = __builtin_nanf("");
-        }
-        const size_t unit = (size_t)b * Hq + hq0 + h;
-        if (single) {
-            const float inv = 1.0f / L;
-            u32 *o = reinterpret_cast<u32 *>(p.out) + (unit * D + d2) / 2;
-            *o = pack_out<QT>(o0 * inv, o1 * inv);
-        } else {
-            const size_t pu = unit * p.num_partitions + part;
-            float2 *po = reinterpret_cast<float2 *>(p.part_o + pu * D + d2);
-            *po = make_float2(o0, o1);
-            if (d2 == 0)
-                *reinterpret_cast<float2 *>(p.part_ml + pu * 2) = make_float2(M, L);
-        }
+        for (int pg = 0; pg < PPT; ++pg)
+            ph_cur[pg] = ph_nxt[pg];
+        ks_cur = ks_nxt;
+        vs_cur = vs_nxt;
+        cur = nxt;
     }
 }
 
-// ---- the split-K reduce kernel ---------------------------------------------
+// ---- the merge kernel --------------------------------------------------------
 //
-// For a sequence spread over P partitions with partials (m_k, l_k, o_k)
-// (m in log2 units): M = max m_k, L = sum l_k 2^(m_k - M),
-// out = sum o_k 2^(m_k - M) / L.  One workgroup per (query head, sequence).
+// For a segment whose tiles were shared by waves w0..w1, with pieces
+// (m_k, l_k, o_k) (m in log2 units): M = max m_k, L = sum l_k 2^(m_k - M),
+// out = sum o_k 2^(m_k - M) / L.  One workgroup per (query head, sequence);
+// it also writes zeros (NaN for an invalid length) for empty sequences.
 
 template <int D, int QT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(DecodeParams p)
 {
-    constexpr int NG = 256 / D;           // partition groups per workgroup
+    constexpr int C4 = D / 4;            // float4 columns of an o vector
+    constexpr int NG = 256 / C4;         // pieces accumulated side by side
     __shared__ float s_red[256];
-    __shared__ float s_L[NG];
-    __shared__ float s_o[NG][D];
+    __shared__ float s_w[256];
+    __shared__ float4 s_o[NG][C4];
+    __shared__ long long s_geo[2];
 
     const int h = blockIdx.x, b = blockIdx.y;
-    const int n = p.context_lens[b];
-    if (n < 0 || n > p.max_context_len)
-        return;                           // the partition kernel wrote NaN
-    const int T = p.partition_tokens;
-    const int np_ = (n + T - 1) / T;
-    if (np_ <= 1)
-        return;                           // the partition kernel wrote the output
-    const size_t unit = (size_t)b * p.num_q_heads + h;
-    const float *ml = p.part_ml + unit * p.num_partitions * 2;
-    const float *po = p.part_o + unit * p.num_partitions * D;
     const int tid = threadIdx.x;
+    const int Hkv = p.num_kv_heads, G = p.num_q_heads / p.num_kv_heads;
+    const int g = h / G, hh = h % G;
+    const size_t unit = (size_t)b * p.num_q_heads + h;
+    const int n = p.context_lens[b];
+    const int nt = tiles_of(n, p.max_context_len);
+    if (nt == 0) {                       // empty or invalid sequence
+        const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
+        if (tid < D / 2)
+            reinterpret_cast<u32 *>(p.out)[(unit * D) / 2 + tid] = pack_out<QT>(fill, fill);
+        return;
+    }
+    // global tile range of segment (b, g) and the waves that covered it
+    if (tid < 64) {
+        const int lane = tid;
+        const long long T = (long long)batch_tiles(p, lane) * Hkv;
+        int carry = 0;
+        for (int c = 0; c < b; c += 64) {
+            const int bb = c + lane;
+            carry += wave_sum_int(bb < b ? tiles_of(p.context_lens[bb], p.max_context_len) : 0);
+        }
+        const long long A = (long long)carry * Hkv + (long long)g * nt;
+        const long long NWe = p.num_splits < T ? p.num_splits : T;
+        if (lane == 0) {
+            s_geo[0] = owner_of(A, T, NWe);
+            s_geo[1] = owner_of(A + nt - 1, T, NWe);
+        }
+    }
+    __syncthreads();
+    const long long w0 = s_geo[0], w1 = s_geo[1];
+    if (w0 == w1)
+        return;                          // one wave owned the segment and wrote it
+    const int np_ = (int)(w1 - w0 + 1);
+    const size_t seg = (size_t)b * Hkv + g;
+    const size_t first = (seg + (size_t)w0) * G + hh;   // piece index of wave w0; then + G per wave
+    const float *ml = p.part_ml;
+    const float4 *po = reinterpret_cast<const float4 *>(p.part_o);
 
     float mx = -INFINITY;
     for (int k = tid; k < np_; k += 256)
-        mx = fmaxf(mx, ml[2 * k]);
+        mx = fmaxf(mx, ml[(first + (size_t)k * G) * 2]);
     s_red[tid] = mx;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
@@ -566,29 +782,55 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DecodeParams p)
         __syncthreads();
     }
     const float M = s_red[0];
-
-    const int d = tid % D, grp = tid / D;
-    float L = 0.0f, o = 0.0f;
-    for (int k = grp; k < np_; k += NG) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * k] - M);
-        L = fmaf(f, ml[2 * k + 1], L);
-        o = fmaf(f, po[(size_t)k * D + d], o);
-    }
-    s_o[grp][d] = o;
-    if (d == 0)
-        s_L[grp] = L;
     __syncthreads();
-    if (tid < D / 2) {
-        float Lt = 0.0f, a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NG; ++q) {
-            Lt += s_L[q];
-            a0 += s_o[q][2 * tid];
-            a1 += s_o[q][2 * tid + 1];
+
+    const int c = tid % C4, grp = tid / C4;
+    float L = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = 0; base < np_; base += 256) {
+        const int k = base + tid;
+        float wk = 0.0f;
+        if (k < np_) {
+            const float2 v = *reinterpret_cast<const float2 *>(ml + (first + (size_t)k * G) * 2);
+            wk = __builtin_amdgcn_exp2f(v.x - M);
+            L = fmaf(wk, v.y, L);
         }
-        const float inv = 1.0f / Lt;
-        u32 *out = reinterpret_cast<u32 *>(p.out) + (unit * D) / 2 + tid;
-        *out = pack_out<QT>(a0 * inv, a1 * inv);
+        s_w[tid] = wk;
+        __syncthreads();
+        const int cnt = min(256, np_ - base);
+#pragma unroll 8
+        for (int kk = grp; kk < cnt; kk += NG) {
+            const float wkk = s_w[kk];
+            const float4 v = po[(first + (size_t)(base + kk) * G) * C4 + c];
+            o.x = fmaf(wkk, v.x, o.x);
+            o.y = fmaf(wkk, v.y, o.y);
+            o.z = fmaf(wkk, v.z, o.z);
+            o.w = fmaf(wkk, v.w, o.w);
+        }
+        __syncthreads();
+    }
+    s_red[tid] = L;
+    s_o[grp][c] = o;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s)
+            s_red[tid] += s_red[tid + s];
+        __syncthreads();
+    }
+    if (tid < C4) {
+        float4 a = s_o[0][tid];
+#pragma unroll
+        for (int q = 1; q < NG; ++q) {
+            const float4 v = s_o[q][tid];
+            a.x += v.x;
+            a.y += v.y;
+            a.z += v.z;
+            a.w += v.w;
+        }
+        const float inv = 1.0f / s_red[0];
+        u32 *out = reinterpret_cast<u32 *>(p.out) + (unit * D) / 2 + 2 * tid;
+        out[0] = pack_out<QT>(a.x * inv, a.y * inv);
+        out[1] = pack_out<QT>(a.z * inv, a.w * inv);
     }
 }
 
@@ -627,10 +869,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteParams p)
 template <int D, int PS, int G, int QT, int KVT>
 int launch_one(const DecodeParams &p, hipStream_t stream)
 {
-    dim3 grid((unsigned)p.num_partitions, (unsigned)p.num_kv_heads, (unsigned)p.batch);
+    dim3 grid((unsigned)p.num_splits);
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    return (int)hipLaunchKernel((const void *)&paged_decode_kernel<D, PS, G, QT, KVT>, grid,
-                                dim3(kWaves * 64), args, 0, stream);
+    return (int)hipLaunchKernel((const void *)&paged_decode_kernel<D, PS, G, QT, KVT>, grid, dim3(64),
+                                args, 0, stream);
 }
 
 template <int D, int PS, int G>

@@ -13,10 +13,10 @@ namespace pkv {
 void clear_error();
 pkv_status fail(pkv_status code, const char *msg);
 
-// Tokens per wave-iteration of the decode kernel and waves per workgroup.
+// Tokens per wave-iteration of the decode kernel; default waves per compute
+// unit of the persistent grid.
 constexpr int kTileTokens = 64;
-constexpr int kWaves = 4;
-constexpr int kDefaultPartitionTokens = 512;
+constexpr int kDefaultWavesPerCU = 8;
 
 enum DType : int { F16 = 0, BF16 = 1, I8 = 2 };
 
@@ -30,17 +30,16 @@ struct DecodeParams {
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
-    float *part_o;     // [batch][Hq][P][D]
-    float *part_ml;    // [batch][Hq][P][2]: (max in log2 units, sum)
+    float *part_o;     // [(segments + num_splits) * G][D] pieces
+    float *part_ml;    // [(segments + num_splits) * G][2]: (max in log2 units, sum)
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t num_pages;
     int32_t max_blocks;
     int32_t max_context_len;
-    int32_t partition_tokens;
-    int32_t num_partitions;
-    float scale_log2;  // softmax scale * log2(e)
+    int32_t num_splits;   // waves of the persistent grid
+    float scale_log2;     // softmax scale * log2(e)
 };
 
 struct WriteParams {

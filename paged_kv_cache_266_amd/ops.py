@@ -47,7 +47,7 @@ def _check_tensor(t, name, device, ndim=None):
 
 def decode_args(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
                 max_context_len: int, out=None, k_scale=None, v_scale=None,
-                workspace=None, partition_tokens: int = 0) -> DecodeArgs:
+                workspace=None, num_splits: int = 0) -> DecodeArgs:
     """Fill the C argument struct from tensors (no device work)."""
     import torch
 
@@ -73,7 +73,7 @@ def decode_args(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
     a.page_size, a.num_pages = PS, num_pages
     a.max_blocks = block_tables.shape[1]
     a.max_context_len = int(max_context_len)
-    a.partition_tokens = int(partition_tokens)
+    a.num_splits = int(num_splits)
     a.q_dtype = DTYPE_CODES[_dtype_name(q)]
     a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
     a.scale = float(scale)
@@ -99,14 +99,15 @@ def alloc_workspace(args: DecodeArgs, device):
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
                       max_context_len: int, out=None, k_scale=None, v_scale=None,
-                      workspace=None, partition_tokens: int = 0, stream=None):
+                      workspace=None, num_splits: int = 0, stream=None):
     """Single-token decode attention over a paged KV cache.
 
     q [B][Hq][D] f16/bf16; k_pool, v_pool [num_pages][Hkv][PS][D] of the same
     type as q or int8 (then k_scale, v_scale [num_pages][Hkv][PS] fp32);
     block_tables [B][max_blocks] int32; context_lens [B] int32 (device).
-    ``max_context_len`` is a host-side bound on context_lens (it sizes the
-    split-K grid).  Returns ``out`` [B][Hq][D] in q's dtype.
+    ``max_context_len`` is a host-side bound on context_lens.  ``num_splits``
+    is the number of waves sharing the batch's tiles (0 = library default).
+    Returns ``out`` [B][Hq][D] in q's dtype.
     """
     import torch
 
@@ -114,7 +115,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         out = torch.empty_like(q)
     a = decode_args(q, k_pool, v_pool, block_tables, context_lens, scale,
                     max_context_len=max_context_len, out=out, k_scale=k_scale, v_scale=v_scale,
-                    workspace=workspace, partition_tokens=partition_tokens)
+                    workspace=workspace, num_splits=num_splits)
     if workspace is None:
         workspace = alloc_workspace(a, q.device)
         a.workspace = _ptr(workspace)

@@ -49,7 +49,6 @@ class Config:
     lens_kind: str        # "fixed" | "uniform" | "lognormal"
     lens_args: Tuple      # fixed: the lengths; uniform: (lo, hi) inclusive;
                           # lognormal: (median, sigma, lo, hi)
-    partition_tokens: int = 512
 
     @property
     def group(self) -> int:

@@ -26,7 +26,7 @@ def small_config(Hq, Hkv, D, qd, kvd, PS, lens, num_pages=None):
                       lens_kind="fixed", lens_args=tuple(lens))
 
 
-def gpu_decode(case, partition_tokens=0, dev=None, max_context_len=None):
+def gpu_decode(case, num_splits=0, dev=None, max_context_len=None):
     """Run pkv_paged_attn_decode on the case; returns the output tensor."""
     import torch
 
@@ -37,7 +37,7 @@ def gpu_decode(case, partition_tokens=0, dev=None, max_context_len=None):
     mcl = cfg.max_context_len if max_context_len is None else max_context_len
     out = pkv.paged_attn_decode(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens,
                                 case.scale, max_context_len=mcl, k_scale=dev.k_scale,
-                                v_scale=dev.v_scale, partition_tokens=partition_tokens)
+                                v_scale=dev.v_scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return out
 

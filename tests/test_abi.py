@@ -48,7 +48,7 @@ def good_args(**kw):
     a.workspace_bytes = 1 << 30
     a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = 4, 32, 8, 128
     a.page_size, a.num_pages, a.max_blocks, a.max_context_len = 64, 1024, 64, 4096
-    a.partition_tokens = 0
+    a.num_splits = 0
     a.q_dtype = a.kv_dtype = _lib.PKV_BF16
     a.scale = 0.088
     for k, v in kw.items():
@@ -78,7 +78,7 @@ def test_valid_arguments_pass_validation():
     (dict(out=FAKE + 8), _lib.PKV_ERR_INVALID_ARG),              # misaligned
     (dict(max_context_len=4097), _lib.PKV_ERR_INVALID_ARG),      # > max_blocks * page_size
     (dict(batch=-1), _lib.PKV_ERR_INVALID_ARG),
-    (dict(partition_tokens=100), _lib.PKV_ERR_INVALID_ARG),
+    (dict(num_splits=-1), _lib.PKV_ERR_INVALID_ARG),
     (dict(workspace=None), _lib.PKV_ERR_WORKSPACE),
     (dict(workspace_bytes=16), _lib.PKV_ERR_WORKSPACE),
 ])
@@ -94,16 +94,19 @@ def test_invalid_arguments_are_rejected_before_launch(change, code):
 def test_workspace_sizes():
     L = _lib.lib()
     n = ctypes.c_size_t()
-    a = good_args(max_context_len=512)
+    a = good_args(num_splits=100)
+    assert L.pkv_decode_num_splits(ctypes.byref(a)) == 100
     assert L.pkv_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
-    assert n.value == 0                      # one partition: no partials
-    a = good_args(max_context_len=4096)      # 8 partitions of 512
-    assert L.pkv_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
-    o = 4 * 32 * 8 * 128 * 4
-    assert n.value == ((o + 255) // 256) * 256 + 4 * 32 * 8 * 2 * 4
-    assert L.pkv_decode_partition_tokens(ctypes.byref(a)) == 512
-    a.partition_tokens = 1024
-    assert L.pkv_decode_partition_tokens(ctypes.byref(a)) == 1024
+    pieces = (4 * 8 + 100) * 4                # (segments + waves) x group
+    o = pieces * 128 * 4
+    assert n.value == ((o + 255) // 256) * 256 + pieces * 2 * 4
+    # never more waves than the batch can have tiles: 4 seqs x 8 heads x 64 tiles
+    a.num_splits = 10 ** 6
+    assert L.pkv_decode_num_splits(ctypes.byref(a)) == 4 * 8 * 64
+    a.num_splits = 0                          # default: 8 per compute unit (>= 1)
+    assert L.pkv_decode_num_splits(ctypes.byref(a)) >= 1
+    a = good_args(batch=0)
+    assert L.pkv_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_write_kv_rejects_bad_arguments():
@@ -120,7 +123,7 @@ def test_write_kv_rejects_bad_arguments():
 
 @pytest.mark.skipif(_lib.lib().pkv_device_count() > 0, reason="a GPU is present")
 def test_launch_without_a_device_reports_device_error():
-    a = good_args(max_context_len=256)   # valid; no workspace needed
+    a = good_args(max_context_len=256)   # valid arguments
     rc = _lib.lib().pkv_paged_attn_decode(ctypes.byref(a), None)
     assert rc == _lib.PKV_ERR_DEVICE
     assert _lib.lib().pkv_last_error().decode()

@@ -47,7 +47,9 @@ def test_parity_full_config(name):
 
 # ---------------------------------------------------------------------------
 # Every compiled instantiation on small ragged batches that span several
-# 64-token tiles, several partitions and a partial last page.
+# 64-token tiles and a partial last page, with the batch's tiles split over
+# the default grid, over 3 waves (segments cut across waves) and over 40
+# waves (about one tile each, many pieces per segment).
 
 SUPPORTED = [(D, PS, G, qd, kvd)
              for D, PS, G in itertools.product((64, 128), (16, 64), (1, 2, 4, 8))
@@ -61,9 +63,9 @@ def test_parity_every_instantiation(D, PS, G, qd, kvd):
     cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, lens)
     note(f"[inst] D={D} PS={PS} G={G} q={qd} kv={kvd} lens={lens}")
     case = make_case(cfg, seed=100 + D + PS + G)
-    for T in (0, 256):     # default partition (one partition here) and split
-        out = gpu_decode(case, partition_tokens=T)
-        compare(case, out, f"T={T}")
+    for splits in (0, 3, 40):
+        out = gpu_decode(case, num_splits=splits)
+        compare(case, out, f"splits={splits}")
 
 
 def test_edge_lengths():
@@ -114,13 +116,13 @@ def test_run_to_run_determinism_bitwise():
 
 def test_split_and_unsplit_agree():
     cfg = small_config(32, 8, 128, "bf16", "bf16", 64, (4096, 3000, 777, 64))
-    note("[split] partitions 256 / 512 / 1024 / 4096")
+    note("[split] 1 / 7 / 64 / 2000 waves and the default")
     case = make_case(cfg, seed=21)
     dev = upload(case, "cuda")
-    outs = {T: to_f64(gpu_decode(case, partition_tokens=T, dev=dev)) for T in (256, 512, 1024, 4096)}
-    for T, o in outs.items():
-        assert np.abs(o - outs[4096]).max() <= 1.6e-2, T
-        compare(case, gpu_decode(case, partition_tokens=T, dev=dev), f"T={T}")
+    outs = {n: to_f64(gpu_decode(case, num_splits=n, dev=dev)) for n in (1, 7, 64, 2000, 0)}
+    for n, o in outs.items():
+        assert np.abs(o - outs[1]).max() <= 1.6e-2, n
+        compare(case, gpu_decode(case, num_splits=n, dev=dev), f"splits={n}")
 
 
 def test_gqa_equals_mha_with_repeated_kv():
