@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -67,16 +69,43 @@ static int32_t resolve_splits(const pkv_decode_args *a)
     return (int32_t)std::min<int64_t>(std::min<int64_t>(want, upper), 1 << 24);
 }
 
-// Workspace: one piece slot per (segment + wave), G query heads each.
+// Workspace layout: a 256-byte header (the tag of the last decode launch),
+// one 16-byte geometry record per (sequence, KV head) segment, then one piece
+// slot per (segment + wave) and query head: head_dim fp32 values, and a
+// (max, sum) pair.
+struct WorkspaceLayout {
+    size_t geo, part_o, part_ml, total;
+};
+
+static WorkspaceLayout workspace_layout(const pkv_decode_args *a, int32_t splits)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t S = (size_t)a->batch * (size_t)a->num_kv_heads;
+    const size_t G = (size_t)(a->num_q_heads / a->num_kv_heads);
+    const size_t pieces = (S + (size_t)splits) * G;
+    WorkspaceLayout L;
+    L.geo = 256;
+    L.part_o = L.geo + up(S * 16);
+    L.part_ml = L.part_o + up(pieces * (size_t)a->head_dim * sizeof(float));
+    L.total = L.part_ml + pieces * 2 * sizeof(float);
+    return L;
+}
+
 static size_t workspace_bytes(const pkv_decode_args *a)
 {
-    if (a->batch == 0)
-        return 0;
-    const size_t G = (size_t)(a->num_q_heads / a->num_kv_heads);
-    const size_t pieces = ((size_t)a->batch * (size_t)a->num_kv_heads + (size_t)resolve_splits(a)) * G;
-    const size_t o = pieces * (size_t)a->head_dim * sizeof(float);
-    const size_t ml = pieces * 2 * sizeof(float);
-    return ((o + 255) & ~(size_t)255) + ml;
+    return a->batch == 0 ? 0 : workspace_layout(a, resolve_splits(a)).total;
+}
+
+// A nonzero 32-bit value that differs from call to call.
+static uint32_t next_tag()
+{
+    static std::atomic<uint32_t> counter{
+        (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
+    uint32_t t;
+    do
+        t = counter.fetch_add(1, std::memory_order_relaxed) * 2654435761u + 0x9E3779B9u;
+    while (t == 0);
+    return t;
 }
 
 // Shape, dtype and pointer checks; no GPU access.
@@ -138,14 +167,16 @@ static DecodeParams make_params(const pkv_decode_args *a)
     p.max_blocks = a->max_blocks;
     p.max_context_len = a->max_context_len;
     p.num_splits = resolve_splits(a);
+    p.tag = next_tag();
     // log2(e) folded into the scale once, in fp32, so the kernels use exp2
     p.scale_log2 = a->scale * 1.44269504088896340736f;
     if (a->workspace) {
-        const size_t G = (size_t)(a->num_q_heads / a->num_kv_heads);
-        const size_t pieces = ((size_t)a->batch * (size_t)a->num_kv_heads + (size_t)p.num_splits) * G;
-        const size_t o = pieces * (size_t)a->head_dim * sizeof(float);
-        p.part_o = (float *)a->workspace;
-        p.part_ml = (float *)((char *)a->workspace + ((o + 255) & ~(size_t)255));
+        const WorkspaceLayout L = workspace_layout(a, p.num_splits);
+        char *ws = (char *)a->workspace;
+        p.ws_tag = (uint32_t *)ws;
+        p.seg_geo = (int4 *)(ws + L.geo);
+        p.part_o = (float *)(ws + L.part_o);
+        p.part_ml = (float *)(ws + L.part_ml);
     }
     return p;
 }

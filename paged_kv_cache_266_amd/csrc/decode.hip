@@ -384,6 +384,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     if (w >= NWe)
         return;
     const long long lo = range_start(w, T, NWe), hi = range_start(w + 1, T, NWe);
+    if (w == 0 && lane == 0)
+        *p.ws_tag = p.tag;               // the merge kernel reads which call it follows
 
     // ---- the tile cursor: sequence b (length n, tiles nt), KV head g, tile k
     struct Cursor {
@@ -532,6 +534,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     bool piece_from_start = cur.k == 0;
 
     for (long long t = lo; t < hi; ++t) {
+        // the wave holding a segment's first tile records which waves share it
+        if (cur.k == 0 && lane == 0)
+            p.seg_geo[cur.b * Hkv + cur.g] =
+                make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
         const bool last_in_range = t + 1 == hi;
         const Cursor nxt = last_in_range ? cur : advance(cur);
         const bool seg_end = last_in_range || nxt.k == 0;
@@ -719,118 +725,107 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 //
 // For a segment whose tiles were shared by waves w0..w1, with pieces
 // (m_k, l_k, o_k) (m in log2 units): M = max m_k, L = sum l_k 2^(m_k - M),
-// out = sum o_k 2^(m_k - M) / L.  One workgroup per (query head, sequence);
-// it also writes zeros (NaN for an invalid length) for empty sequences.
+// out = sum o_k 2^(m_k - M) / L.  One workgroup per (query head, sequence).  The
+// decode kernel recorded (tag, w0, w1) for every segment it started; a
+// segment one wave covered whole (w0 == w1) is already written.  An empty
+// sequence gets zeros (NaN for an invalid length).  Four waves take every
+// fourth piece each, merging online with several pieces' loads in flight,
+// and combine through LDS.
 
 template <int D, int QT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(DecodeParams p)
 {
-    constexpr int C4 = D / 4;            // float4 columns of an o vector
-    constexpr int NG = 256 / C4;         // pieces accumulated side by side
-    __shared__ float s_red[256];
-    __shared__ float s_w[256];
-    __shared__ float4 s_o[NG][C4];
-    __shared__ long long s_geo[2];
+    constexpr int DPL = D / 64;          // output dims per lane
+    constexpr int WAVES = 4, UNROLL = 4;
+    __shared__ float s_m[WAVES], s_l[WAVES];
+    __shared__ float s_acc[WAVES][D];
 
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int Hkv = p.num_kv_heads, G = p.num_q_heads / p.num_kv_heads;
     const int g = h / G, hh = h % G;
     const size_t unit = (size_t)b * p.num_q_heads + h;
     const int n = p.context_lens[b];
     const int nt = tiles_of(n, p.max_context_len);
-    if (nt == 0) {                       // empty or invalid sequence
+    if (nt == 0) {
         const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
-        if (tid < D / 2)
-            reinterpret_cast<u32 *>(p.out)[(unit * D) / 2 + tid] = pack_out<QT>(fill, fill);
+        if (threadIdx.x < D / 2)
+            reinterpret_cast<u32 *>(p.out)[(unit * D) / 2 + threadIdx.x] = pack_out<QT>(fill, fill);
         return;
     }
-    // global tile range of segment (b, g) and the waves that covered it
-    if (tid < 64) {
-        const int lane = tid;
-        const long long T = (long long)batch_tiles(p, lane) * Hkv;
-        int carry = 0;
-        for (int c = 0; c < b; c += 64) {
-            const int bb = c + lane;
-            carry += wave_sum_int(bb < b ? tiles_of(p.context_lens[bb], p.max_context_len) : 0);
-        }
-        const long long A = (long long)carry * Hkv + (long long)g * nt;
-        const long long NWe = p.num_splits < T ? p.num_splits : T;
-        if (lane == 0) {
-            s_geo[0] = owner_of(A, T, NWe);
-            s_geo[1] = owner_of(A + nt - 1, T, NWe);
-        }
-    }
-    __syncthreads();
-    const long long w0 = s_geo[0], w1 = s_geo[1];
-    if (w0 == w1)
-        return;                          // one wave owned the segment and wrote it
-    const int np_ = (int)(w1 - w0 + 1);
     const size_t seg = (size_t)b * Hkv + g;
-    const size_t first = (seg + (size_t)w0) * G + hh;   // piece index of wave w0; then + G per wave
-    const float *ml = p.part_ml;
-    const float4 *po = reinterpret_cast<const float4 *>(p.part_o);
+    const int4 geo = p.seg_geo[seg];
+    if ((uint32_t)geo.x != *p.ws_tag || geo.y >= geo.z)
+        return;                          // covered whole by one wave: already written
+    const int np_ = geo.z - geo.y + 1;
+    const size_t first = (seg + (size_t)geo.y) * G + hh;   // wave w0's piece; + G per wave
 
-    float mx = -INFINITY;
-    for (int k = tid; k < np_; k += 256)
-        mx = fmaxf(mx, ml[(first + (size_t)k * G) * 2]);
-    s_red[tid] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s)
-            s_red[tid] = fmaxf(s_red[tid], s_red[tid + s]);
-        __syncthreads();
-    }
-    const float M = s_red[0];
-    __syncthreads();
-
-    const int c = tid % C4, grp = tid / C4;
-    float L = 0.0f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int base = 0; base < np_; base += 256) {
-        const int k = base + tid;
-        float wk = 0.0f;
-        if (k < np_) {
-            const float2 v = *reinterpret_cast<const float2 *>(ml + (first + (size_t)k * G) * 2);
-            wk = __builtin_amdgcn_exp2f(v.x - M);
-            L = fmaf(wk, v.y, L);
-        }
-        s_w[tid] = wk;
-        __syncthreads();
-        const int cnt = min(256, np_ - base);
-#pragma unroll 8
-        for (int kk = grp; kk < cnt; kk += NG) {
-            const float wkk = s_w[kk];
-            const float4 v = po[(first + (size_t)(base + kk) * G) * C4 + c];
-            o.x = fmaf(wkk, v.x, o.x);
-            o.y = fmaf(wkk, v.y, o.y);
-            o.z = fmaf(wkk, v.z, o.z);
-            o.w = fmaf(wkk, v.w, o.w);
-        }
-        __syncthreads();
-    }
-    s_red[tid] = L;
-    s_o[grp][c] = o;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s)
-            s_red[tid] += s_red[tid + s];
-        __syncthreads();
-    }
-    if (tid < C4) {
-        float4 a = s_o[0][tid];
+    // online merge of this wave's pieces (k = wave, wave + 4, ...), UNROLL
+    // pieces' loads in flight at a time
+    float m = -INFINITY, L = 0.0f, acc[DPL];
 #pragma unroll
-        for (int q = 1; q < NG; ++q) {
-            const float4 v = s_o[q][tid];
-            a.x += v.x;
-            a.y += v.y;
-            a.z += v.z;
-            a.w += v.w;
+    for (int d = 0; d < DPL; ++d)
+        acc[d] = 0.0f;
+    for (int k0 = wave; k0 < np_; k0 += WAVES * UNROLL) {
+        float2 ml[UNROLL];
+        float ov[UNROLL][DPL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int k = k0 + u * WAVES;
+            const size_t pc = first + (size_t)(k < np_ ? k : 0) * G;
+            ml[u] = *reinterpret_cast<const float2 *>(p.part_ml + pc * 2);
+#pragma unroll
+            for (int d = 0; d < DPL; ++d)
+                ov[u][d] = p.part_o[pc * D + DPL * lane + d];
+            if (k >= np_)
+                ml[u].x = -INFINITY;
         }
-        const float inv = 1.0f / s_red[0];
-        u32 *out = reinterpret_cast<u32 *>(p.out) + (unit * D) / 2 + 2 * tid;
-        out[0] = pack_out<QT>(a.x * inv, a.y * inv);
-        out[1] = pack_out<QT>(a.z * inv, a.w * inv);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (ml[u].x == -INFINITY)
+                continue;
+            const float m_new = fmaxf(m, ml[u].x);
+            const float a = __builtin_amdgcn_exp2f(m - m_new), c = __builtin_amdgcn_exp2f(ml[u].x - m_new);
+            L = L * a + ml[u].y * c;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d)
+                acc[d] = acc[d] * a + ov[u][d] * c;
+            m = m_new;
+        }
+    }
+    if (lane == 0) {
+        s_m[wave] = m;
+        s_l[wave] = L;
+    }
+#pragma unroll
+    for (int d = 0; d < DPL; ++d)
+        s_acc[wave][DPL * lane + d] = acc[d];
+    __syncthreads();
+    if (wave == 0) {
+        float M = s_m[0];
+#pragma unroll
+        for (int q = 1; q < WAVES; ++q)
+            M = fmaxf(M, s_m[q]);
+        float Lt = 0.0f, o[DPL];
+#pragma unroll
+        for (int d = 0; d < DPL; ++d)
+            o[d] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < WAVES; ++q) {
+            const float f = __builtin_amdgcn_exp2f(s_m[q] - M);   // 0 for a wave without pieces
+            Lt = fmaf(f, s_l[q], Lt);
+#pragma unroll
+            for (int d = 0; d < DPL; ++d)
+                o[d] = fmaf(f, s_acc[q][DPL * lane + d], o[d]);
+        }
+        const float inv = 1.0f / Lt;
+        if constexpr (DPL == 2) {
+            reinterpret_cast<u32 *>(p.out)[(unit * D) / 2 + lane] = pack_out<QT>(o[0] * inv, o[1] * inv);
+        } else {
+            const float other = __shfl_xor(o[0], 1);
+            if ((lane & 1) == 0)
+                reinterpret_cast<u32 *>(p.out)[(unit * D) / 2 + lane / 2] = pack_out<QT>(o[0] * inv, other * inv);
+        }
     }
 }
 

@@ -2,6 +2,8 @@
 // libpagedkv.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include <cstddef>
 #include <cstdint>
 
@@ -30,6 +32,8 @@ struct DecodeParams {
     const int32_t *block_tables;
     const int32_t *context_lens;
     void *out;
+    uint32_t *ws_tag;  // workspace header: tag of the last decode launch
+    int4 *seg_geo;     // [segments]: (tag, first wave, last wave, 0) of each segment
     float *part_o;     // [(segments + num_splits) * G][D] pieces
     float *part_ml;    // [(segments + num_splits) * G][2]: (max in log2 units, sum)
     int32_t batch;
@@ -39,6 +43,7 @@ struct DecodeParams {
     int32_t max_blocks;
     int32_t max_context_len;
     int32_t num_splits;   // waves of the persistent grid
+    uint32_t tag;         // nonzero, different for every call
     float scale_log2;     // softmax scale * log2(e)
 };
 

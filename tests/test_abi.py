@@ -97,9 +97,11 @@ def test_workspace_sizes():
     a = good_args(num_splits=100)
     assert L.pkv_decode_num_splits(ctypes.byref(a)) == 100
     assert L.pkv_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
-    pieces = (4 * 8 + 100) * 4                # (segments + waves) x group
-    o = pieces * 128 * 4
-    assert n.value == ((o + 255) // 256) * 256 + pieces * 2 * 4
+    segments = 4 * 8
+    pieces = (segments + 100) * 4             # (segments + waves) x group
+    up = lambda x: (x + 255) // 256 * 256
+    # header, per-segment geometry records, piece vectors, piece (max, sum) pairs
+    assert n.value == 256 + up(segments * 16) + up(pieces * 128 * 4) + pieces * 2 * 4
     # never more waves than the batch can have tiles: 4 seqs x 8 heads x 64 tiles
     a.num_splits = 10 ** 6
     assert L.pkv_decode_num_splits(ctypes.byref(a)) == 4 * 8 * 64
