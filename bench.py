@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+COPY_CALIBRATION_MIB = 1024   # size of the plain copy the counters are calibrated on
 DEFAULT_CONFIG = "llama3_8b_gqa"
 
 
@@ -44,8 +45,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of COPY_CALIBRATION_MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                              "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this benchmark and "
+                         "of the copy calibration into profiles/paged_decode_<config>_counters.json")
     return ap.parse_args()
 
 
@@ -71,6 +76,51 @@ def traffic_from_profile(workload: str):
     if rec.get("source_digest") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path, counter):
+    import csv
+
+    with open(path, newline="") as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def _per_dispatch(rows, match):
+    """Counter value (KiB) per dispatch of kernels whose name contains match."""
+    vals = {}
+    for r in rows:
+        if match in r["Kernel_Name"]:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def summarize_counters(workload: str, files, copy_bytes: int) -> dict:
+    """HBM bytes per launch of paged_decode_kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each divided by what the same counter
+    reads per byte for a plain device copy of copy_bytes bytes."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = files
+    fetch = _per_dispatch(_counter_rows(fetch_csv, "FETCH_SIZE"), "paged_decode_kernel")
+    write = _per_dispatch(_counter_rows(write_csv, "WRITE_SIZE"), "paged_decode_kernel")
+    # the copy kernel is the largest dispatch of the calibration run
+    cf = max(_per_dispatch(_counter_rows(cfetch_csv, "FETCH_SIZE"), ""))
+    cw = max(_per_dispatch(_counter_rows(cwrite_csv, "WRITE_SIZE"), ""))
+    f_factor = cf * 1024 / copy_bytes
+    w_factor = cw * 1024 / copy_bytes
+    fetch_b = sum(fetch) / len(fetch) * 1024 / f_factor
+    write_b = sum(write) / len(write) * 1024 / w_factor
+    return {
+        "workload": workload,
+        "kernel": "paged_decode_kernel",
+        "source_digest": source_digest(),
+        "dispatches": {"fetch": len(fetch), "write": len(write)},
+        "fetch_kib_per_dispatch": round(sum(fetch) / len(fetch), 1),
+        "write_kib_per_dispatch": round(sum(write) / len(write), 1),
+        "copy_bytes": copy_bytes,
+        "copy_factor": {"fetch": round(f_factor, 4), "write": round(w_factor, 4)},
+        "hbm_fetch_bytes_per_launch": int(fetch_b),
+        "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+    }
 
 
 def copy_calibration(mib: int) -> None:
@@ -121,6 +171,19 @@ def cpu_baseline(case, min_seconds: float):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        from synth import CONFIGS, make_case
+
+        rec = summarize_counters(args.config, args.summarize_counters, COPY_CALIBRATION_MIB << 20)
+        rec["bytes_alg_per_launch"] = make_case(CONFIGS[args.config]).bytes_alg()
+        rec["traffic_over_alg"] = round(rec["hbm_bytes_per_launch"] / rec["bytes_alg_per_launch"], 4)
+        path = os.path.join(ROOT, "profiles", f"paged_decode_{args.config}_counters.json")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -129,8 +192,8 @@ def main():
     import numpy as np
     import torch
 
-    if args.copy_calibration_mib:
-        copy_calibration(args.copy_calibration_mib)
+    if args.copy_calibration:
+        copy_calibration(COPY_CALIBRATION_MIB)
         return
 
     import paged_kv_cache_266_amd as pkv
@@ -175,16 +238,16 @@ def main():
         a.workspace_bytes = 0 if ws is None else ws.numel()
     num_splits = L.pkv_decode_num_splits(ctypes.byref(argv[0]))
 
-    def step(i, ev=None):
+    def step(i):
+        check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
+
+    def step_timed(i, ev):
         a = ctypes.byref(argv[i % rotate])
-        if ev is not None:
-            ev[0].record(stream)
+        ev[0].record(stream)
         check(L.pkv_paged_attn_decode_partitions(a, sh))
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         check(L.pkv_splitk_reduce(a, sh))
-        if ev is not None:
-            ev[2].record(stream)
+        ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -198,19 +261,26 @@ def main():
     max_err = float(np.abs(got - ref).max())
     tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}[cfg.kv_dtype]
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: K whole steps (one library call each), nothing else
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    value = bytes_alg / (ms_per_step * 1e-3) / 1e9
 
+    # a second pass of K steps with HIP events on the launch stream around
+    # each kernel: per-kernel durations for the roofline
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step_timed(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     red_ms = step_ms - part_ms
-    ms_per_step = wall_ms / args.steps
-    value = bytes_alg / (ms_per_step * 1e-3) / 1e9
 
     achieved = bytes_alg / (part_ms.mean() * 1e-3) / 1e9
     traffic = traffic_from_profile(cfg.name)
