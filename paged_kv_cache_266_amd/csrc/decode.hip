@@ -219,6 +219,18 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int voff)
     return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0);
 }
 
+// The tile cursor is the same on every lane, but the compiler cannot prove
+// it; a buffer descriptor built from a per-lane value costs a loop over the
+// distinct values around every load.  Reading the address from the first
+// active lane puts it in scalar registers.
+__device__ __forceinline__ const char *uniform_ptr(const char *ptr)
+{
+    const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, kBufferFlags);
@@ -261,7 +273,7 @@ struct TileAddr {
     {
 #pragma unroll
         for (int pg = 0; pg < S::PPT; ++pg)
-            base[pg] = head + (size_t)(ph[pg] >= 0 ? ph[pg] : 0) * page_stride;
+            base[pg] = uniform_ptr(head + (size_t)(ph[pg] >= 0 ? ph[pg] : 0) * page_stride);
         // token i*TPI + r exists iff i*TPI + r < rem
         nvalid = rem > r ? (rem - r + S::TPI - 1) / S::TPI : 0;
     }
