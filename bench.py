@@ -1,16 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of paged single-token decode attention on one MI355X.
 
-One step = one decode call over every sequence of one layer (the decode
-kernel, whose persistent grid splits the batch's tiles evenly over its waves,
-then the merge kernel), on synthetic inputs already resident in HBM.  Layers are rotated
+One step = one decode call over every sequence of one layer (one kernel
+launch: a persistent grid that splits the batch's tiles evenly over its waves
+and merges shared sequences in-kernel), on synthetic inputs already resident
+in HBM.  Layers are rotated
 (distinct pool buffers with the same contents) so the 256 MB Infinity Cache
 cannot serve a layer from the previous step.
 
 Prints ONE JSON line: value = algorithmic HBM bytes per step / time per step
-(GB/s), with the per-kernel roofline of the partition kernel (timed with HIP
-events on the stream it runs on) and the fp64 oracle timed on this host's
-cores as a baseline.
+(GB/s), with the roofline of the decode kernel (timed with HIP events on the
+stream it runs on) and the fp64 oracle timed on this host's cores as a
+baseline.
 
     python bench.py [--steps K] [--warmup W] [--config NAME]
 """
@@ -29,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 COPY_CALIBRATION_MIB = 1024   # size of the plain copy the counters are calibrated on
+WARMUP_SECONDS = 0.25         # minimum untimed warm-up after the W warm-up steps
 DEFAULT_CONFIG = "llama3_8b_gqa"
 
 
@@ -233,24 +235,31 @@ def main():
                             num_splits=args.num_splits)
         argv.append(a)
     ws = pkv.alloc_workspace(argv[0], q.device)
+    ctr = pkv.alloc_merge_counters(argv[0], q.device)
     for a in argv:
         a.workspace = 0 if ws is None else ws.data_ptr()
         a.workspace_bytes = 0 if ws is None else ws.numel()
+        a.merge_counters = 0 if ctr is None else ctr.data_ptr()
+        a.merge_counter_bytes = 0 if ctr is None else 4 * ctr.numel()
     num_splits = L.pkv_decode_num_splits(ctypes.byref(argv[0]))
 
     def step(i):
         check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
 
     def step_timed(i, ev):
-        a = ctypes.byref(argv[i % rotate])
         ev[0].record(stream)
-        check(L.pkv_paged_attn_decode_partitions(a, sh))
+        check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
         ev[1].record(stream)
-        check(L.pkv_splitk_reduce(a, sh))
-        ev[2].record(stream)
 
-    for i in range(args.warmup):
+    # W warm-up steps, then more (untimed) until the GPU has been busy for
+    # WARMUP_SECONDS, so that clocks have settled before the timed region
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t_w < WARMUP_SECONDS:
         step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # parity of the benchmarked launch configuration against the oracle
@@ -272,17 +281,15 @@ def main():
     value = bytes_alg / (ms_per_step * 1e-3) / 1e9
 
     # a second pass of K steps with HIP events on the launch stream around
-    # each kernel: per-kernel durations for the roofline
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # each call (one kernel launch): the kernel's duration for the roofline
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step_timed(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
-    part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
-    red_ms = step_ms - part_ms
+    kern_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
 
-    achieved = bytes_alg / (part_ms.mean() * 1e-3) / 1e9
+    achieved = bytes_alg / (kern_ms.mean() * 1e-3) / 1e9
     traffic = traffic_from_profile(cfg.name)
     result = {
         "metric": "paged-attn decode HBM GB/s (% of 8 TB/s peak), us per layer-step",
@@ -307,12 +314,11 @@ def main():
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-        "event_us": {
-            "step_median": round(float(np.median(step_ms)) * 1e3, 2),
-            "step_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
-            "step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
-            "partition_kernel_mean": round(float(part_ms.mean()) * 1e3, 2),
-            "merge_kernel_mean": round(float(red_ms.mean()) * 1e3, 2),
+        "kernel_event_us": {
+            "mean": round(float(kern_ms.mean()) * 1e3, 2),
+            "median": round(float(np.median(kern_ms)) * 1e3, 2),
+            "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+            "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
         },
         "roofline": {
             "bound": "hbm",

@@ -178,9 +178,20 @@ typedef struct pkv_decode_args {
                                    sequence, including the one just appended; the
                                    single query attends to all of them.             */
     void *out;                  /* device [batch][num_q_heads][head_dim], q_dtype    */
-    void *workspace;            /* device scratch of >= pkv_decode_workspace_bytes;
-                                   may be NULL when that size is 0                  */
+    void *workspace;            /* device scratch of >= pkv_decode_workspace_bytes,
+                                   256-byte aligned; its contents between calls do
+                                   not matter; may be NULL when that size is 0     */
     size_t workspace_bytes;
+    uint32_t *merge_counters;   /* device array of >= pkv_decode_counter_bytes bytes,
+                                   4-byte aligned, ZERO-FILLED once when allocated
+                                   and used for nothing else: the arrival counters
+                                   of the in-kernel merge.  Every complete call
+                                   leaves all of it zero again, whatever the
+                                   shapes, so one array serves any later calls
+                                   that do not overlap in time.  Only
+                                   pkv_paged_attn_decode uses it (NULL is fine for
+                                   the two-launch form).                             */
+    size_t merge_counter_bytes;
     int32_t batch;              /* >= 0; 0 is a no-op                               */
     int32_t num_q_heads;
     int32_t num_kv_heads;       /* divides num_q_heads; group = Hq / Hkv in {1,2,4,8} */
@@ -193,27 +204,35 @@ typedef struct pkv_decode_args {
     int32_t num_splits;         /* waves sharing the batch: the batch's 64-token tiles
                                    (all sequences, all KV heads) are divided into this
                                    many equal contiguous shares, one per wave of a
-                                   persistent grid.  0 = library default (8 per compute
-                                   unit); always capped at the number of tiles the
-                                   batch can have.                                   */
+                                   persistent grid.  0 = library default (4 waves per
+                                   compute unit for 16-bit KV, 8 for int8 KV);
+                                   always capped at the number of tiles the batch
+                                   can have.                                         */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16; out has the same type       */
     pkv_dtype kv_dtype;         /* PKV_F16 (with f16 q), PKV_BF16 (with bf16 q), or
                                    PKV_I8 (with either)                              */
     float scale;                /* softmax scale applied to q.k (e.g. 1/sqrt(head_dim)) */
 } pkv_decode_args;
 
-/* Bytes of workspace pkv_paged_attn_decode needs for these arguments: one
+/* Bytes of workspace the decode calls need for these arguments: one
  * (max, sum, head_dim-vector) slot per query head for every (sequence, KV
- * head) segment plus every wave, fp32 (uses batch, num_q_heads, num_kv_heads,
- * head_dim, max_context_len, num_splits).  0 only for an empty batch. */
+ * head) segment plus every wave, fp32, one 16-byte record per segment and a
+ * 256-byte header (uses batch, num_q_heads, num_kv_heads, head_dim,
+ * max_context_len, num_splits).  0 only for an empty batch. */
 pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *args, size_t *bytes);
+
+/* Bytes of merge_counters pkv_paged_attn_decode needs for these arguments:
+ * 4 x (segments + waves) x levels, with levels the depth of a fan-in-8 tree
+ * over the waves (uses batch, num_kv_heads, max_context_len, num_splits).
+ * 0 only for an empty batch. */
+pkv_status pkv_decode_counter_bytes(const pkv_decode_args *args, size_t *bytes);
 
 /* Number of waves the library uses for these arguments (resolves 0). */
 int32_t pkv_decode_num_splits(const pkv_decode_args *args);
 
 /* Checks the arguments without touching the GPU (pointer presence and
- * 16-byte alignment, shapes, dtype pair, workspace size).  Returns what
- * pkv_paged_attn_decode would return before launching. */
+ * 16-byte alignment, shapes, dtype pair, workspace and counter sizes).
+ * Returns what pkv_paged_attn_decode would return before launching. */
 pkv_status pkv_decode_validate(const pkv_decode_args *args);
 
 /* out[b][h][:] = softmax_t(scale * q[b][h] . K_t) . V_t over the
@@ -222,16 +241,21 @@ pkv_status pkv_decode_validate(const pkv_decode_args *args);
  * whose context length is negative or above max_context_len, or whose block
  * table names a page outside [0, num_pages), gets NaN in every element of its
  * output instead of a memory access outside the pools.
- * Two launches on `stream`: the decode kernel (a persistent grid of
- * num_splits waves, each streaming an equal share of the batch's tiles; a
- * sequence/head a wave covers whole is written directly, the pieces of one
- * shared by several waves go to the workspace) and the merge kernel (combines
- * pieces; writes the outputs of empty sequences).  Stateless and re-entrant;
- * the workspace must not be shared by concurrent calls. */
+ * One launch on `stream`: a persistent grid of num_splits waves, each
+ * streaming an equal share of the batch's tiles.  A (sequence, KV head) a
+ * wave covers whole is written directly; the pieces of one shared by several
+ * waves go to the workspace and the last wave to finish a group of pieces
+ * merges them (a fan-in-8 tree; no wave ever waits for another).  The result
+ * does not depend on the order in which waves finish.  Stateless and
+ * re-entrant; the workspace must not be shared by calls that may overlap. */
 pkv_status pkv_paged_attn_decode(const pkv_decode_args *args, void *stream);
 
-/* The two launches of pkv_paged_attn_decode, separately (same arguments and
- * workspace).  Calling both in order on one stream is pkv_paged_attn_decode. */
+/* The same computation in two launches: the decode kernel leaves every piece
+ * of a shared segment in the workspace (it merges nothing), and the merge
+ * kernel combines them, one workgroup per (query head, sequence).  Calling
+ * both in order on one stream gives the result of pkv_paged_attn_decode up to
+ * fp32 rounding order.  This form is for callers that combine pieces
+ * themselves or time the phases apart; it does not use the counters. */
 pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *args, void *stream);
 pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
 

@@ -30,7 +30,8 @@ EXPORTED = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_alloc", "pkv_append_tokens",
     "pkv_seq_release", "pkv_seq_info", "pkv_seq_pages", "pkv_free_page_count",
     "pkv_free_pages", "pkv_build_block_tables", "pkv_kv_bytes",
-    "pkv_decode_workspace_bytes", "pkv_decode_num_splits", "pkv_decode_validate",
+    "pkv_decode_workspace_bytes", "pkv_decode_counter_bytes", "pkv_decode_num_splits",
+    "pkv_decode_validate",
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
     "pkv_write_kv",
 ]
@@ -48,6 +49,7 @@ class DecodeArgs(ctypes.Structure):
         ("block_tables", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("merge_counters", ctypes.c_void_p), ("merge_counter_bytes", ctypes.c_size_t),
         ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),

@@ -59,13 +59,15 @@ static int device_cu_count()
     return cus;
 }
 
-// Waves of the persistent grid: the caller's choice or 8 per compute unit,
-// never more than the batch can have tiles (at least 1).
+// Waves of the persistent grid: the caller's choice or the default per
+// compute unit for the KV type, never more than the batch can have tiles
+// (at least 1).
 static int32_t resolve_splits(const pkv_decode_args *a)
 {
     const int64_t tiles_per_seq = ((int64_t)a->max_context_len + kTileTokens - 1) / kTileTokens;
     const int64_t upper = std::max<int64_t>(1, (int64_t)a->batch * a->num_kv_heads * tiles_per_seq);
-    const int64_t want = a->num_splits > 0 ? a->num_splits : (int64_t)kDefaultWavesPerCU * device_cu_count();
+    const int64_t per_cu = a->kv_dtype == PKV_I8 ? kDefaultWavesPerCU8 : kDefaultWavesPerCU16;
+    const int64_t want = a->num_splits > 0 ? a->num_splits : per_cu * device_cu_count();
     return (int32_t)std::min<int64_t>(std::min<int64_t>(want, upper), 1 << 24);
 }
 
@@ -76,6 +78,15 @@ static int32_t resolve_splits(const pkv_decode_args *a)
 struct WorkspaceLayout {
     size_t geo, part_o, part_ml, total;
 };
+
+// Levels of the fan-in-8 merge tree needed for up to `splits` waves per segment.
+static int merge_levels(int32_t splits)
+{
+    int levels = 1;
+    for (int64_t span = 8; span < splits; span *= 8)
+        ++levels;
+    return levels;
+}
 
 static WorkspaceLayout workspace_layout(const pkv_decode_args *a, int32_t splits)
 {
@@ -96,6 +107,17 @@ static size_t workspace_bytes(const pkv_decode_args *a)
     return a->batch == 0 ? 0 : workspace_layout(a, resolve_splits(a)).total;
 }
 
+// Arrival counters of the in-kernel merge: one per piece slot (segment +
+// wave) per level of the merge tree.
+static size_t counter_bytes(const pkv_decode_args *a)
+{
+    if (a->batch == 0)
+        return 0;
+    const int32_t splits = resolve_splits(a);
+    const size_t S = (size_t)a->batch * (size_t)a->num_kv_heads;
+    return (size_t)merge_levels(splits) * (S + (size_t)splits) * sizeof(uint32_t);
+}
+
 // A nonzero 32-bit value that differs from call to call.
 static uint32_t next_tag()
 {
@@ -109,7 +131,7 @@ static uint32_t next_tag()
 }
 
 // Shape, dtype and pointer checks; no GPU access.
-static pkv_status validate(const pkv_decode_args *a)
+static pkv_status validate(const pkv_decode_args *a, bool one_launch)
 {
     if (!a)
         return fail(PKV_ERR_INVALID_ARG, "decode: null argument struct");
@@ -146,6 +168,11 @@ static pkv_status validate(const pkv_decode_args *a)
     if (need > 0 && (!a->workspace || a->workspace_bytes < need || ((uintptr_t)a->workspace & 255u)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace missing, smaller than "
                                        "pkv_decode_workspace_bytes, or not 256-byte aligned");
+    const size_t need_ctr = one_launch ? counter_bytes(a) : 0;
+    if (need_ctr > 0 && (!a->merge_counters || a->merge_counter_bytes < need_ctr ||
+                         ((uintptr_t)a->merge_counters & 3u)))
+        return fail(PKV_ERR_WORKSPACE, "decode: merge_counters missing, smaller than "
+                                       "pkv_decode_counter_bytes, or not 4-byte aligned");
     return PKV_OK;
 }
 
@@ -168,6 +195,8 @@ static DecodeParams make_params(const pkv_decode_args *a)
     p.max_context_len = a->max_context_len;
     p.num_splits = resolve_splits(a);
     p.tag = next_tag();
+    p.fused = 0;
+    p.counters = a->merge_counters;
     // log2(e) folded into the scale once, in fp32, so the kernels use exp2
     p.scale_log2 = a->scale * 1.44269504088896340736f;
     if (a->workspace) {
@@ -224,6 +253,18 @@ extern "C" pkv_status pkv_decode_workspace_bytes(const pkv_decode_args *a, size_
     return PKV_OK;
 }
 
+extern "C" pkv_status pkv_decode_counter_bytes(const pkv_decode_args *a, size_t *bytes)
+{
+    clear_error();
+    if (!a || !bytes)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_decode_counter_bytes: null argument");
+    if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->num_q_heads % a->num_kv_heads ||
+        a->max_context_len < 0 || a->num_splits < 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_decode_counter_bytes: bad sizes");
+    *bytes = counter_bytes(a);
+    return PKV_OK;
+}
+
 extern "C" int32_t pkv_decode_num_splits(const pkv_decode_args *a)
 {
     if (!a || a->batch < 0 || a->num_kv_heads <= 0 || a->max_context_len < 0 || a->num_splits < 0)
@@ -234,13 +275,13 @@ extern "C" int32_t pkv_decode_num_splits(const pkv_decode_args *a)
 extern "C" pkv_status pkv_decode_validate(const pkv_decode_args *a)
 {
     clear_error();
-    return validate(a);
+    return validate(a, true);
 }
 
 extern "C" pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *a, void *stream)
 {
     clear_error();
-    pkv_status st = validate(a);
+    pkv_status st = validate(a, false);
     if (st != PKV_OK || a->batch == 0)
         return st;
     DecodeParams p = make_params(a);
@@ -252,7 +293,7 @@ extern "C" pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *a,
 extern "C" pkv_status pkv_splitk_reduce(const pkv_decode_args *a, void *stream)
 {
     clear_error();
-    pkv_status st = validate(a);
+    pkv_status st = validate(a, false);
     if (st != PKV_OK || a->batch == 0)
         return st;
     DecodeParams p = make_params(a);
@@ -263,18 +304,14 @@ extern "C" pkv_status pkv_splitk_reduce(const pkv_decode_args *a, void *stream)
 extern "C" pkv_status pkv_paged_attn_decode(const pkv_decode_args *a, void *stream)
 {
     clear_error();
-    pkv_status st = validate(a);
+    pkv_status st = validate(a, true);
     if (st != PKV_OK || a->batch == 0)
         return st;
     DecodeParams p = make_params(a);
+    p.fused = 1;   // one launch: the decode kernel merges shared segments itself
     int err = launch_decode_partitions(p, a->head_dim, a->page_size, a->num_q_heads / a->num_kv_heads,
                                        a->q_dtype, a->kv_dtype, stream);
-    if (err)
-        return device_fail(err, "pkv_paged_attn_decode (partition kernel)");
-    err = launch_splitk_reduce(p, a->head_dim, a->q_dtype, stream);
-    if (err)
-        return device_fail(err, "pkv_paged_attn_decode (merge kernel)");
-    return PKV_OK;
+    return err ? device_fail(err, "pkv_paged_attn_decode") : PKV_OK;
 }
 
 extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)

@@ -28,8 +28,8 @@
 //    then V of tile t, then K of tile t+1: each chunk's V load is issued as
 //    soon as its K has been used and the next tile's K as soon as its V has
 //    been used, so a tile of K/V is always in flight behind the arithmetic,
-//    across segment boundaries too (the next segment's q is fetched a tile
-//    ahead).
+//    across segment boundaries too (the next segment's q is fetched behind
+//    the next tile's K loads).
 //  * q.k.  Lane (row r, column j) holds 16 bytes of one token row and the
 //    matching slice of each of the G query heads of the group; dot2
 //    instructions (f16/bf16) or byte conversions + FMAs (int8) give partial
@@ -45,7 +45,9 @@
 //    (broadcast reads) and accumulates G x (elements per lane) fp32 sums.
 //  * Combine.  Token rows are summed across lanes.  A segment a wave covers
 //    whole is written directly; the pieces of a segment shared by waves go to
-//    the workspace as (max, sum, unnormalised output) for the merge kernel.
+//    the workspace as (max, sum, unnormalised output) and are merged, after
+//    the main loop, by the last wave to finish each group of them (or, in the
+//    two-launch form, by the merge kernel).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -231,9 +233,59 @@ __device__ __forceinline__ const char *uniform_ptr(const char *ptr)
     return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ float *uniform_fptr(float *ptr)
+{
+    return const_cast<float *>(reinterpret_cast<const float *>(uniform_ptr(reinterpret_cast<const char *>(ptr))));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, kBufferFlags);
+}
+
+// Pieces of shared segments travel between waves that may run on different
+// XCDs (each with its own L2).  They are written and read with system-
+// coherent accesses (sc0 sc1: written through to memory, read from memory),
+// so no device-wide cache write-back or invalidate is needed; a writer waits
+// for its stores to complete before it counts its arrival.
+constexpr int kCoherent = 1 | 16;
+
+__device__ __forceinline__ void store_coherent4(float *base, int bytes, int voff, float4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), tile_rsrc((const char *)base, bytes),
+                                           voff, 0, kCoherent);
+}
+
+__device__ __forceinline__ void store_coherent2(float *base, int bytes, int voff, float2 v)
+{
+    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), tile_rsrc((const char *)base, bytes),
+                                          voff, 0, kCoherent);
+}
+
+__device__ __forceinline__ float4 load_coherent4(const float *base, int bytes, int voff)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc((const char *)base, bytes),
+                                                                            voff, 0, kCoherent));
+}
+
+__device__ __forceinline__ float2 load_coherent2(const float *base, int bytes, int voff)
+{
+    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(tile_rsrc((const char *)base, bytes),
+                                                                           voff, 0, kCoherent));
+}
+
+__device__ __forceinline__ float load_coherent1(const float *base, int bytes, int voff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc((const char *)base, bytes),
+                                                                          voff, 0, kCoherent));
+}
+
+__device__ __forceinline__ void store_coherent1(float *base, int bytes, int voff, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), tile_rsrc((const char *)base, bytes), voff,
+                                          0, kCoherent);
 }
 
 // ---- the partition kernel ---------------------------------------------------
@@ -373,6 +425,132 @@ __device__ __forceinline__ void locate(const DecodeParams &p, long long t, int l
     start_out = 0;
 }
 
+// ---- merging the pieces of a shared segment, inside the decode kernel -------
+//
+// The n waves w0 .. w0+n-1 that share a segment each leave a piece
+// (m, l, o) -- running max in log2 units, sum of exponentials, unnormalised
+// output -- in piece slot (segment + wave).  They are merged up a tree of
+// fan-in 8 without any wave waiting for another: at level L the pieces form
+// blocks of 8 children, a per-block counter counts arrivals, and the wave
+// whose arrival completes a block merges its children (in slot order, so
+// the result does not depend on which wave arrived last) into the block's
+// first slot, then arrives at the next level.  The merge of the top block
+// writes the normalised output.  Counters wrap to zero on the arrival that
+// completes them (atomic increment modulo the child count), so a zeroed
+// workspace is zero again after every call.
+//
+// Ordering: pieces are written and read with system-coherent accesses, a
+// wave's stores have completed before its arrival is counted (a system-scope
+// atomic), and the merging wave reads only after its own count returned.
+
+template <int D, int G, int QT>
+__device__ __forceinline__ void settle_piece(const DecodeParams &p, int seg, int w0, int n, int w, int lane)
+{
+    constexpr int LPH = 64 / G;     // lanes per query head
+    constexpr int DPL = D / LPH;    // output dims per lane
+    constexpr int FAN = 8;
+    const int h = lane / LPH, d0 = (lane % LPH) * DPL;
+    const size_t slot0 = (size_t)seg + (size_t)w0;
+    const size_t level_stride = (size_t)p.batch * p.num_kv_heads + (size_t)p.num_splits;
+    int k = w - w0;
+    int span = 1;
+    for (int level = 0; span < n; ++level, span *= FAN) {
+        const int parent = k - k % (span * FAN);
+        const int children = min(FAN, (n - parent + span - 1) / span);
+        if (children > 1) {
+            // this wave's stores (the piece, or the block it merged) complete
+            // before its arrival is counted
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(0);
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __builtin_amdgcn_atomic_inc32(p.counters + level * level_stride + slot0 + parent,
+                                                    (uint32_t)(children - 1), __ATOMIC_RELAXED, "");
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old != (uint32_t)(children - 1))
+                return;               // a later arrival completes this block
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+            float mc[FAN], lc[FAN], oc[FAN][DPL];
+#pragma unroll
+            for (int c = 0; c < FAN; ++c) {
+                const size_t slot = slot0 + parent + (size_t)(c < children ? c : 0) * span;
+                const float2 ml = load_coherent2(uniform_fptr(p.part_ml + slot * G * 2), G * 8, h * 8);
+                mc[c] = c < children ? ml.x : -INFINITY;
+                lc[c] = ml.y;
+                const float *src = uniform_fptr(p.part_o + slot * G * D);
+                if constexpr (DPL % 4 == 0) {
+#pragma unroll
+                    for (int v = 0; v < DPL / 4; ++v) {
+                        const float4 x = load_coherent4(src, G * D * 4, (h * D + d0 + 4 * v) * 4);
+                        oc[c][4 * v] = x.x;
+                        oc[c][4 * v + 1] = x.y;
+                        oc[c][4 * v + 2] = x.z;
+                        oc[c][4 * v + 3] = x.w;
+                    }
+                } else if constexpr (DPL == 2) {
+                    const float2 x = load_coherent2(src, G * D * 4, (h * D + d0) * 4);
+                    oc[c][0] = x.x;
+                    oc[c][1] = x.y;
+                } else {
+                    oc[c][0] = load_coherent1(src, G * D * 4, (h * D + d0) * 4);
+                }
+            }
+            float M = mc[0];
+#pragma unroll
+            for (int c = 1; c < FAN; ++c)
+                M = fmaxf(M, mc[c]);
+            float L = 0.0f, acc[DPL];
+#pragma unroll
+            for (int x = 0; x < DPL; ++x)
+                acc[x] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < FAN; ++c) {
+                if (c < children) {
+                    const float f = __builtin_amdgcn_exp2f(mc[c] - M);
+                    L = fmaf(f, lc[c], L);
+#pragma unroll
+                    for (int x = 0; x < DPL; ++x)
+                        acc[x] = fmaf(f, oc[c][x], acc[x]);
+                }
+            }
+            if (span * FAN >= n) {
+                // top of the tree: the normalised output of query head g*G + h
+                const int b = seg / p.num_kv_heads, g = seg % p.num_kv_heads;
+                const size_t unit = (size_t)b * p.num_q_heads + (size_t)g * G + h;
+                const float inv = 1.0f / L;
+                u32 *dst = reinterpret_cast<u32 *>(p.out) + (unit * D + d0) / 2;
+                if constexpr (DPL >= 2) {
+#pragma unroll
+                    for (int x = 0; x < DPL / 2; ++x)
+                        dst[x] = pack_out<QT>(acc[2 * x] * inv, acc[2 * x + 1] * inv);
+                } else {
+                    const float other = __shfl_xor(acc[0], 1);
+                    if ((lane & 1) == 0)
+                        dst[0] = pack_out<QT>(acc[0] * inv, other * inv);
+                }
+                return;
+            }
+            // the block's result replaces its first child
+            const size_t slot = slot0 + parent;
+            float *dst = uniform_fptr(p.part_o + slot * G * D);
+            if constexpr (DPL % 4 == 0) {
+#pragma unroll
+                for (int v = 0; v < DPL / 4; ++v)
+                    store_coherent4(dst, G * D * 4, (h * D + d0 + 4 * v) * 4,
+                                    make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]));
+            } else if constexpr (DPL == 2) {
+                store_coherent2(dst, G * D * 4, (h * D + d0) * 4, make_float2(acc[0], acc[1]));
+            } else {
+                store_coherent1(dst, G * D * 4, (h * D + d0) * 4, acc[0]);
+            }
+            if (lane % LPH == 0)
+                store_coherent2(uniform_fptr(p.part_ml + slot * G * 2), G * 8, h * 8, make_float2(M, L));
+        }
+        k = parent;
+    }
+}
+
 // ---- the partition kernel ---------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -391,6 +569,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     const long long NW = gridDim.x, w = blockIdx.x;
 
     const long long T = (long long)batch_tiles(p, lane) * Hkv;
+    // a sequence without tiles (empty, or an invalid length) has no wave
+    // streaming it: its outputs are written here, zeros (NaN if invalid)
+    for (long long b = w; b < p.batch; b += NW) {
+        const int n = p.context_lens[b];
+        if (tiles_of(n, p.max_context_len) == 0) {
+            const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
+            u32 *o = reinterpret_cast<u32 *>(p.out) + (size_t)b * Hq * D / 2;
+            for (int i = lane; i < Hq * D / 2; i += 64)
+                o[i] = pack_out<QT>(fill, fill);
+        }
+    }
     // waves beyond the tile count idle, so every working wave's range is non-empty
     const long long NWe = NW < T ? NW : T;
     if (w >= NWe)
@@ -402,6 +591,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // ---- the tile cursor: sequence b (length n, tiles nt), KV head g, tile k
     struct Cursor {
         int b, n, nt, g, k;
+        // the cursor is the same on every lane; keep it in scalar registers
+        __device__ __forceinline__ void make_uniform()
+        {
+            b = __builtin_amdgcn_readfirstlane(b);
+            n = __builtin_amdgcn_readfirstlane(n);
+            nt = __builtin_amdgcn_readfirstlane(nt);
+            g = __builtin_amdgcn_readfirstlane(g);
+            k = __builtin_amdgcn_readfirstlane(k);
+        }
     };
     Cursor cur;
     {
@@ -412,6 +610,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const long long off = lo - start;
         cur.g = (int)(off / cur.nt);
         cur.k = (int)(off % cur.nt);
+        cur.make_uniform();
     }
     auto advance = [&](const Cursor &c) {
         Cursor x = c;
@@ -428,6 +627,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 } while (x.nt == 0 && x.b < p.batch);
             }
         }
+        x.make_uniform();
         return x;
     };
 
@@ -537,13 +737,25 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     u32x4 ring[R];
     [&]<int... I>(std::integer_sequence<int, I...>) { ((ring[I] = ka.template load<I>(lane_off)), ...); }
         (std::make_integer_sequence<int, R>{});
-    u32 qraw[G][QW];
-    load_q(cur, qraw);
-    set_q(qraw);
+    // int8 KV: the next segment's raw q is fetched a tile ahead (its fp32
+    // form takes longer to set up)
+    u32 qraw[kI8 ? G : 1][QW];
+    {
+        u32 q0[G][QW];
+        load_q(cur, q0);
+        set_q(q0);
+    }
     reset_state();
     float ks_cur, vs_cur, ks_nxt = 1.0f, vs_nxt = 1.0f;
     own_scales(cur, ph_cur, ks_cur, vs_cur);
     bool piece_from_start = cur.k == 0;
+    // Pieces of shared segments this wave wrote (at most two: the segment its
+    // range starts in and the one it ends in) are settled after the loop; the
+    // records (segment, first wave, wave count) wait in LDS, not registers.
+    __shared__ int s_pend[2][3];
+    __shared__ int s_npend;
+    if (lane == 0)
+        s_npend = 0;
 
     for (long long t = lo; t < hi; ++t) {
         // the wave holding a segment's first tile records which waves share it
@@ -559,9 +771,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
             for (int pg = 0; pg < PPT; ++pg)
                 ph_nxt[pg] = -1;
-        // next segment's q goes out now; it is used after this tile
-        if (seg_end && !last_in_range)
-            load_q(nxt, qraw);
+        if constexpr (kI8) {
+            if (seg_end && !last_in_range)
+                load_q(nxt, qraw);
+        }
 
         // ---- q.k: partial dots of chunk i, folded into the reduce-scatter
         // tree as they come; chunk i's registers then take V of this tile
@@ -703,24 +916,47 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                         for (int v = 0; v < EPL / 8; ++v)
                             o[v] = u32x4{packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]};
                     } else {
-                        const size_t piece = ((size_t)seg + (size_t)w) * G + h;
-                        float4 *po = reinterpret_cast<float4 *>(p.part_o + piece * D + EPL * j);
+                        // piece group of slot (seg + w): G heads x D values, G (m, l) pairs
+                        const size_t slot = (size_t)seg + (size_t)w;
+                        float *po = uniform_fptr(p.part_o + slot * G * D);
 #pragma unroll
                         for (int v = 0; v < EPL / 4; ++v)
-                            po[v] = any_bad ? make_float4(nan, nan, nan, nan)
-                                            : make_float4(acc[h][4 * v], acc[h][4 * v + 1], acc[h][4 * v + 2],
-                                                          acc[h][4 * v + 3]);
+                            store_coherent4(po, G * D * 4, (h * D + EPL * j + 4 * v) * 4,
+                                            any_bad ? make_float4(nan, nan, nan, nan)
+                                                    : make_float4(acc[h][4 * v], acc[h][4 * v + 1],
+                                                                  acc[h][4 * v + 2], acc[h][4 * v + 3]));
                         if (j == 0)
-                            *reinterpret_cast<float2 *>(p.part_ml + piece * 2) =
-                                make_float2(m_run[h], any_bad ? nan : lt);
+                            store_coherent2(uniform_fptr(p.part_ml + slot * G * 2), G * 8, h * 8,
+                                            make_float2(m_run[h], any_bad ? nan : lt));
                     }
+                }
+            }
+            if (!whole) {
+                const long long first = t - cur.k;   // the segment's first global tile
+                const int w0 = (int)owner_of(first, T, NWe);
+                const int w1 = (int)owner_of(first + cur.nt - 1, T, NWe);
+                if (lane == 0) {
+                    const int i = s_npend;
+                    s_pend[i][0] = seg;
+                    s_pend[i][1] = w0;
+                    s_pend[i][2] = w1 - w0 + 1;
+                    s_npend = i + 1;
                 }
             }
             reset_state();
             any_bad = false;
             piece_from_start = true;
-            if (!last_in_range)
-                set_q(qraw);
+            if (!last_in_range) {
+                if constexpr (kI8) {
+                    set_q(qraw);   // loaded a tile ahead
+                } else {
+                    // the next segment's q: loaded now, behind the next
+                    // tile's K loads already in flight, so it arrives with them
+                    u32 qn[G][QW];
+                    load_q(nxt, qn);
+                    set_q(qn);
+                }
+            }
         }
 
         // ---- roll the window forward
@@ -730,6 +966,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         ks_cur = ks_nxt;
         vs_cur = vs_nxt;
         cur = nxt;
+    }
+
+    if (p.fused) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int npend = __builtin_amdgcn_readfirstlane(s_npend);
+        for (int i = 0; i < npend; ++i)
+            settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),
+                                   __builtin_amdgcn_readfirstlane(s_pend[i][1]),
+                                   __builtin_amdgcn_readfirstlane(s_pend[i][2]), (int)w, lane);
     }
 }
 

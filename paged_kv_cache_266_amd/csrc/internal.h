@@ -15,10 +15,15 @@ namespace pkv {
 void clear_error();
 pkv_status fail(pkv_status code, const char *msg);
 
-// Tokens per wave-iteration of the decode kernel; default waves per compute
-// unit of the persistent grid.
+// Tokens per wave-iteration of the decode kernel.
 constexpr int kTileTokens = 64;
-constexpr int kDefaultWavesPerCU = 8;
+// Default waves per compute unit of the persistent grid (measured on
+// MI355X): one per SIMD for 16-bit KV, where a second co-resident wave on a
+// SIMD only slows the first (and the grid ends on the slower one); two per
+// SIMD for int8 KV, whose conversions leave more arithmetic to overlap with
+// memory latency.
+constexpr int kDefaultWavesPerCU16 = 4;
+constexpr int kDefaultWavesPerCU8 = 8;
 
 enum DType : int { F16 = 0, BF16 = 1, I8 = 2 };
 
@@ -36,6 +41,7 @@ struct DecodeParams {
     int4 *seg_geo;     // [segments]: (tag, first wave, last wave, 0) of each segment
     float *part_o;     // [(segments + num_splits) * G][D] pieces
     float *part_ml;    // [(segments + num_splits) * G][2]: (max in log2 units, sum)
+    uint32_t *counters;  // [merge levels][segments + num_splits] arrival counters, zero between calls
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -44,6 +50,7 @@ struct DecodeParams {
     int32_t max_context_len;
     int32_t num_splits;   // waves of the persistent grid
     uint32_t tag;         // nonzero, different for every call
+    int32_t fused;        // 1: the decode kernel merges shared segments itself
     float scale_log2;     // softmax scale * log2(e)
 };
 

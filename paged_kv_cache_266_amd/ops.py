@@ -47,7 +47,7 @@ def _check_tensor(t, name, device, ndim=None):
 
 def decode_args(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
                 max_context_len: int, out=None, k_scale=None, v_scale=None,
-                workspace=None, num_splits: int = 0) -> DecodeArgs:
+                workspace=None, merge_counters=None, num_splits: int = 0) -> DecodeArgs:
     """Fill the C argument struct from tensors (no device work)."""
     import torch
 
@@ -69,6 +69,8 @@ def decode_args(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
     a.out = _ptr(out)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.merge_counters = _ptr(merge_counters)
+    a.merge_counter_bytes = 0 if merge_counters is None else merge_counters.numel() * merge_counters.element_size()
     a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = B, Hq, Hkv, D
     a.page_size, a.num_pages = PS, num_pages
     a.max_blocks = block_tables.shape[1]
@@ -86,6 +88,12 @@ def workspace_bytes(args: DecodeArgs) -> int:
     return int(n.value)
 
 
+def counter_bytes(args: DecodeArgs) -> int:
+    n = ctypes.c_size_t()
+    check(lib().pkv_decode_counter_bytes(ctypes.byref(args), ctypes.byref(n)), "counter_bytes")
+    return int(n.value)
+
+
 def alloc_workspace(args: DecodeArgs, device):
     """A workspace tensor for these arguments (None when none is needed)."""
     import torch
@@ -97,9 +105,21 @@ def alloc_workspace(args: DecodeArgs, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def alloc_merge_counters(args: DecodeArgs, device, at_least: int = 0):
+    """A zero-filled merge-counter array for these arguments (None when none
+    is needed).  Keep it for later calls: each call leaves it zero again, so
+    it needs no clearing as long as calls using it do not overlap in time."""
+    import torch
+
+    n = max(counter_bytes(args), at_least)
+    if n == 0:
+        return None
+    return torch.zeros((n + 3) // 4, dtype=torch.int32, device=device)
+
+
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, *,
                       max_context_len: int, out=None, k_scale=None, v_scale=None,
-                      workspace=None, num_splits: int = 0, stream=None):
+                      workspace=None, merge_counters=None, num_splits: int = 0, stream=None):
     """Single-token decode attention over a paged KV cache.
 
     q [B][Hq][D] f16/bf16; k_pool, v_pool [num_pages][Hkv][PS][D] of the same
@@ -107,6 +127,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     block_tables [B][max_blocks] int32; context_lens [B] int32 (device).
     ``max_context_len`` is a host-side bound on context_lens.  ``num_splits``
     is the number of waves sharing the batch's tiles (0 = library default).
+    ``workspace`` and ``merge_counters`` are allocated per call when not
+    given (see alloc_workspace, alloc_merge_counters).
     Returns ``out`` [B][Hq][D] in q's dtype.
     """
     import torch
@@ -115,11 +137,15 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         out = torch.empty_like(q)
     a = decode_args(q, k_pool, v_pool, block_tables, context_lens, scale,
                     max_context_len=max_context_len, out=out, k_scale=k_scale, v_scale=v_scale,
-                    workspace=workspace, num_splits=num_splits)
+                    workspace=workspace, merge_counters=merge_counters, num_splits=num_splits)
     if workspace is None:
         workspace = alloc_workspace(a, q.device)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = 0 if workspace is None else workspace.numel()
+    if merge_counters is None:
+        merge_counters = alloc_merge_counters(a, q.device)
+        a.merge_counters = _ptr(merge_counters)
+        a.merge_counter_bytes = 0 if merge_counters is None else 4 * merge_counters.numel()
     check(lib().pkv_paged_attn_decode(ctypes.byref(a), _stream_handle(stream, q.device)),
           "paged_attn_decode")
     return out

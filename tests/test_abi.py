@@ -46,6 +46,8 @@ def good_args(**kw):
     a.q = a.k_pool = a.v_pool = a.block_tables = a.context_lens = a.out = FAKE
     a.workspace = FAKE
     a.workspace_bytes = 1 << 30
+    a.merge_counters = FAKE
+    a.merge_counter_bytes = 1 << 30
     a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = 4, 32, 8, 128
     a.page_size, a.num_pages, a.max_blocks, a.max_context_len = 64, 1024, 64, 4096
     a.num_splits = 0
@@ -91,6 +93,21 @@ def test_invalid_arguments_are_rejected_before_launch(change, code):
         assert getattr(_lib.lib(), fn)(ctypes.byref(a), None) == code
 
 
+@pytest.mark.parametrize("change", [dict(merge_counters=None), dict(merge_counter_bytes=4),
+                                    dict(merge_counters=FAKE + 2)])
+def test_one_launch_form_needs_merge_counters(change):
+    """Only the one-launch call uses the counters; the two-launch form runs
+    without them."""
+    a = good_args(**change)
+    assert validate(a) == _lib.PKV_ERR_WORKSPACE
+    assert _lib.lib().pkv_paged_attn_decode(ctypes.byref(a), None) == _lib.PKV_ERR_WORKSPACE
+    # the two-launch entry points accept these arguments and fail only for
+    # want of a device (not tried where a GPU is present: the pointers are fake)
+    if _lib.lib().pkv_device_count() == 0:
+        for fn in ("pkv_paged_attn_decode_partitions", "pkv_splitk_reduce"):
+            assert getattr(_lib.lib(), fn)(ctypes.byref(a), None) == _lib.PKV_ERR_DEVICE
+
+
 def test_workspace_sizes():
     L = _lib.lib()
     n = ctypes.c_size_t()
@@ -102,13 +119,22 @@ def test_workspace_sizes():
     up = lambda x: (x + 255) // 256 * 256
     # header, per-segment geometry records, piece vectors, piece (max, sum) pairs
     assert n.value == 256 + up(segments * 16) + up(pieces * 128 * 4) + pieces * 2 * 4
+    # merge counters: one per piece slot (segment + wave) and level of a
+    # fan-in-8 tree over 100 waves (8 < 100 <= 512: 3 levels)
+    assert L.pkv_decode_counter_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == 3 * (segments + 100) * 4
+    for waves, levels in ((1, 1), (8, 1), (9, 2), (64, 2), (65, 3), (512, 3), (513, 4)):
+        a.num_splits = waves
+        assert L.pkv_decode_counter_bytes(ctypes.byref(a), ctypes.byref(n)) == 0
+        assert n.value == levels * (segments + waves) * 4, waves
     # never more waves than the batch can have tiles: 4 seqs x 8 heads x 64 tiles
     a.num_splits = 10 ** 6
     assert L.pkv_decode_num_splits(ctypes.byref(a)) == 4 * 8 * 64
-    a.num_splits = 0                          # default: 8 per compute unit (>= 1)
+    a.num_splits = 0                          # default: 4 per compute unit for bf16 KV (>= 1)
     assert L.pkv_decode_num_splits(ctypes.byref(a)) >= 1
     a = good_args(batch=0)
     assert L.pkv_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
+    assert L.pkv_decode_counter_bytes(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_write_kv_rejects_bad_arguments():

@@ -142,6 +142,81 @@ def test_gqa_equals_mha_with_repeated_kv():
     assert np.abs(a - b).max() <= 1.6e-2
 
 
+def _two_launch(case, dev, num_splits=0):
+    """The unfused form: partition kernel, then merge kernel, same workspace."""
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    cfg = case.cfg
+    out = torch.empty_like(dev.q)
+    a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                        max_context_len=cfg.max_context_len, out=out, k_scale=dev.k_scale,
+                        v_scale=dev.v_scale, num_splits=num_splits)
+    ws = pkv.alloc_workspace(a, dev.q.device)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()   # no merge counters needed
+    sh = torch.cuda.current_stream().cuda_stream
+    check(lib().pkv_paged_attn_decode_partitions(ctypes.byref(a), sh))
+    check(lib().pkv_splitk_reduce(ctypes.byref(a), sh))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("lens,splits", [
+    ((4096, 3000, 777, 64, 0, 1), 0),        # ragged GQA batch, default grid
+    ((65536,), 1000),                        # one segment shared by 1000 waves: 4 merge levels
+    ((20000, 9, 20000), 300),
+])
+def test_one_launch_and_two_launch_forms_agree(lens, splits):
+    cfg = small_config(32, 8, 128, "bf16", "bf16", 64, lens)
+    note(f"[fused vs two-launch] lens {lens} splits {splits}")
+    case = make_case(cfg, seed=31)
+    dev = upload(case, "cuda")
+    one = gpu_decode(case, num_splits=splits, dev=dev)
+    two = _two_launch(case, dev, num_splits=splits)
+    compare(case, one, "one launch")
+    compare(case, two, "two launches")
+    assert np.abs(to_f64(one) - to_f64(two)).max() <= 1.6e-2
+
+
+def test_buffers_reused_across_shapes_and_counters_return_to_zero():
+    """One workspace and one merge-counter array serve calls of different
+    shapes in turn; after each, every counter is zero again and every output
+    is right."""
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    note("[buffer reuse] big, small, big, small")
+    big = make_case(small_config(32, 8, 128, "bf16", "bf16", 64, (30000, 5000, 64, 4000)), seed=41)
+    small = make_case(small_config(32, 8, 128, "bf16", "bf16", 64, (700, 65)), seed=42)
+    cases = [big, small, big, small]
+    devs = {id(c): upload(c, "cuda") for c in (big, small)}
+    args = []
+    for c in cases:
+        d = devs[id(c)]
+        out = torch.empty_like(d.q)
+        a = pkv.decode_args(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, c.scale,
+                            max_context_len=c.cfg.max_context_len, out=out, num_splits=600)
+        args.append((c, a, out))
+    ws = pkv.alloc_workspace(args[0][1], "cuda")          # the bigger of the two shapes
+    ws.fill_(0xA5)                                        # contents between calls do not matter
+    ctr = pkv.alloc_merge_counters(args[0][1], "cuda")
+    for c, a, out in args:
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        a.merge_counters, a.merge_counter_bytes = ctr.data_ptr(), 4 * ctr.numel()
+        check(lib().pkv_paged_attn_decode(ctypes.byref(a), torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        compare(c, out, f"B={c.cfg.batch}")
+        assert int(ctr.abs().sum()) == 0
+
+
 def torch_equal_bits(a, b):
     import torch
 
