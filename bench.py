@@ -251,6 +251,18 @@ def main():
         check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
         ev[1].record(stream)
 
+    # parity of the benchmarked launch configuration against the oracle,
+    # checked first: the oracle keeps the GPU idle for seconds, so it must
+    # not sit between the warm-up and the timed region
+    import oracle
+
+    step(0)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    ref = oracle.paged_decode(case)
+    max_err = float(np.abs(got - ref).max())
+    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}[cfg.kv_dtype]
+
     # W warm-up steps, then more (untimed) until the GPU has been busy for
     # WARMUP_SECONDS, so that clocks have settled before the timed region
     t_w = time.perf_counter()
@@ -261,14 +273,6 @@ def main():
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-
-    # parity of the benchmarked launch configuration against the oracle
-    import oracle
-
-    got = out.to(torch.float64).cpu().numpy()
-    ref = oracle.paged_decode(case)
-    max_err = float(np.abs(got - ref).max())
-    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}[cfg.kv_dtype]
 
     # the timed region: K whole steps (one library call each), nothing else
     torch.cuda.synchronize()
