@@ -26,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC_PATH = os.path.join(HERE, "oracle.c")
 
-DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2}
+DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "fp8": 3}
 
 
 def build(verbose: bool = False, src: str = SRC_PATH, out: str = LIB_PATH) -> str:
@@ -54,6 +54,8 @@ def load(path: str):
     L.oracle_f16_to_f64.restype = ctypes.c_double
     L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     L.oracle_bf16_to_f64.restype = ctypes.c_double
+    L.oracle_fp8e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    L.oracle_fp8e4m3_to_f64.restype = ctypes.c_double
     common = [ci, ci, ci, ci, ci, ci, vp, ci, vp, vp, f32p, f32p, i32p, ci, ci,
               i32p, ci, i32p, ctypes.c_float]
     L.oracle_paged_decode.argtypes = common + [f64p, ci]
@@ -187,3 +189,7 @@ def f16_to_f64(bits: int) -> float:
 
 def bf16_to_f64(bits: int) -> float:
     return lib().oracle_bf16_to_f64(bits)
+
+
+def fp8e4m3_to_f64(bits: int) -> float:
+    return lib().oracle_fp8e4m3_to_f64(bits)

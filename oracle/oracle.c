@@ -26,10 +26,11 @@
  *                                                "TensorRT-LLM 深度实战", 3.3
  *
  * Every stored input is decoded exactly into double (f16, bf16, int8 x fp32
- * scale are all exact in fp64) and all arithmetic is fp64.  A sequence with
+ * scale and fp8 e4m3 x fp32 scale are all exact in fp64) and all arithmetic is fp64.  A sequence with
  * n_b == 0 yields zeros.  Where the pages are silent the readings are: pool
  * layout [page][kv_head][slot][dim], contiguous GQA groups, context length
- * counting every cached token, int8 value = scale * code.
+ * counting every cached token, int8 value = scale * code, fp8 value =
+ * scale * e4m3(code).
  *
  * Compiled with -ffp-contract=off so every product and sum rounds as written.
  */
@@ -38,7 +39,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_FP8 = 3 };
 enum { ORC_OK = 0, ORC_BAD_ARG = -1, ORC_BAD_PAGE = -2, ORC_NO_MEM = -3 };
 
 /* IEEE 754 binary16 -> double, exact (normals, subnormals, inf, nan). */
@@ -66,14 +67,39 @@ double oracle_bf16_to_f64(uint16_t b)
     return (double)f;
 }
 
+/* FP8 E4M3 as the OCP 8-bit floating point specification defines it (the
+ * "e4m3fn" encoding): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds subnormals 0.m * 2^-6; S.1111.111 is NaN;
+ * there are no infinities, so the largest magnitude is 1.75 * 2^8 = 448.
+ * Exact in double. */
+double oracle_fp8e4m3_to_f64(uint8_t b)
+{
+    int sign = b >> 7;
+    int e = (b >> 3) & 0xf;
+    int m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);                  /* 0.m * 2^-6 */
+    else
+        v = ldexp((double)(m | 8), e - 10);        /* 1.m * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 static double load_elem(int dtype, const void *base, size_t idx)
 {
     if (dtype == ORC_F16)
         return oracle_f16_to_f64(((const uint16_t *)base)[idx]);
     if (dtype == ORC_BF16)
         return oracle_bf16_to_f64(((const uint16_t *)base)[idx]);
+    if (dtype == ORC_FP8)
+        return oracle_fp8e4m3_to_f64(((const uint8_t *)base)[idx]);
     return (double)((const int8_t *)base)[idx];
 }
+
+/* KV types stored with one fp32 scale per token per KV head. */
+static int scaled_kv(int dtype) { return dtype == ORC_I8 || dtype == ORC_FP8; }
 
 typedef struct {
     int B, Hq, Hkv, D, PS;
@@ -111,7 +137,7 @@ static double kv_elem(const problem *p, int which, long row, int g, int slot, in
     size_t tile = ((size_t)row * p->Hkv + g) * p->PS + slot;
     const void *base = which ? p->v_pages : p->k_pages;
     double x = load_elem(p->kv_dtype, base, tile * p->D + d);
-    if (p->kv_dtype == ORC_I8) {
+    if (scaled_kv(p->kv_dtype)) {
         const float *sc = which ? p->v_scale : p->k_scale;
         x = (double)sc[tile] * x;
     }
@@ -160,7 +186,7 @@ static int check(const problem *p)
         return ORC_BAD_ARG;
     if (p->Hq % p->Hkv)
         return ORC_BAD_ARG;
-    if (p->kv_dtype == ORC_I8 && (!p->k_scale || !p->v_scale))
+    if (scaled_kv(p->kv_dtype) && (!p->k_scale || !p->v_scale))
         return ORC_BAD_ARG;
     return ORC_OK;
 }

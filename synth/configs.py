@@ -42,7 +42,7 @@ class Config:
     num_kv_heads: int
     head_dim: int
     q_dtype: str          # "f16" | "bf16"
-    kv_dtype: str         # "f16" | "bf16" | "i8"
+    kv_dtype: str         # "f16" | "bf16" | "i8" | "fp8" (OCP E4M3)
     page_size: int
     num_pages: int
     seed: int

@@ -12,13 +12,14 @@ from typing import Optional
 
 import numpy as np
 
-from .make import BF16_NAN, F16_NAN, I8_POISON, Case
+from .make import BF16_NAN, F16_NAN, FP8_NAN, I8_POISON, Case
 
 
 def torch_dtype(name: str):
     import torch
 
-    return {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}[name]
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+            "fp8": torch.float8_e4m3fn}[name]
 
 
 @dataclass
@@ -50,13 +51,14 @@ def upload(case: Case, device, poison: Optional[bool] = None) -> DeviceCase:
     poison = case.poison if poison is None else poison
     shape = (cfg.num_pages, cfg.num_kv_heads, cfg.page_size, cfg.head_dim)
     used = torch.from_numpy(case.used_pages.astype(np.int64)).to(device)
-    if cfg.kv_dtype == "i8":
-        fill = int(I8_POISON) if poison else 0
+    if cfg.kv_dtype in ("i8", "fp8"):
+        # byte codes move as raw bytes (index_copy has no fp8 kernel)
+        fill = (int(I8_POISON) if cfg.kv_dtype == "i8" else int(FP8_NAN)) if poison else 0
         pools = []
         for pages in (case.k_pages, case.v_pages):
-            p = torch.full(shape, fill, dtype=torch.int8, device=device)
-            p.index_copy_(0, used, torch.from_numpy(pages).to(device))
-            pools.append(p)
+            p = torch.full(shape, fill & 0xFF, dtype=torch.uint8, device=device)
+            p.index_copy_(0, used, torch.from_numpy(np.ascontiguousarray(pages).view(np.uint8)).to(device))
+            pools.append(p.view(torch_dtype(cfg.kv_dtype)))
         scales = []
         for sc in (case.k_scale, case.v_scale):
             s = torch.full(shape[:3], float("nan") if poison else 0.0,

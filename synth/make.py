@@ -19,7 +19,11 @@ Storage encodings (the inputs both sides consume bit-for-bit):
 * f16 / bf16: round-to-nearest-even from float32;
 * int8 (symmetric, one scale per token per KV head):
   ``s = max(max_d |x_d|, 1e-5) / 127`` in float32 and
-  ``x8 = clip(rint(x / s), -127, 127)``.
+  ``x8 = clip(rint(x / s), -127, 127)``;
+* fp8 (OCP E4M3, one scale per token per KV head):
+  ``s = max(max_d |x_d|, 1e-5) / 448`` in float32 and ``x8 = e4m3(x / s)``,
+  rounded to nearest even by torch's float8_e4m3fn cast (|x / s| <= 448, so
+  nothing saturates).
 
 This module draws and lays out inputs only; no attention arithmetic lives here.
 """
@@ -36,6 +40,7 @@ from .configs import Config
 F16_NAN = np.uint16(0x7E00)
 BF16_NAN = np.uint16(0x7FC0)
 I8_POISON = np.int8(-128)
+FP8_NAN = np.uint8(0x7F)
 
 
 def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -48,6 +53,17 @@ def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
         t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
         return t.view(torch.int16).numpy().view(np.uint16)
     raise ValueError(dtype)
+
+
+def quantize_fp8(x: np.ndarray):
+    """Per-row OCP E4M3 encoding over the last axis: (codes uint8, scales fp32)."""
+    import torch
+
+    amax = np.max(np.abs(x), axis=-1)
+    s = (np.maximum(amax, np.float32(1e-5)) / np.float32(448.0)).astype(np.float32)
+    y = torch.from_numpy(np.ascontiguousarray(x / s[..., None], dtype=np.float32))
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, s
 
 
 def quantize_int8(x: np.ndarray):
@@ -102,10 +118,10 @@ class Case:
         """Bytes the decode step must move per layer: valid K/V (+ scales),
         q in, out, the used block-table entries and the context lengths."""
         c = self.cfg
-        e_kv = 1 if c.kv_dtype == "i8" else 2
+        e_kv = 1 if c.kv_dtype in ("i8", "fp8") else 2
         n = self.context_lens.astype(np.int64)
         kv = int(n.sum()) * c.num_kv_heads * c.head_dim * 2 * e_kv
-        if c.kv_dtype == "i8":
+        if c.kv_dtype in ("i8", "fp8"):
             kv += int(n.sum()) * c.num_kv_heads * 2 * 4
         qo = c.batch * c.num_q_heads * c.head_dim * (2 + 2)
         pages = -(-n // c.page_size)
@@ -142,10 +158,15 @@ def make_case(cfg: Config, seed: Optional[int] = None, poison: bool = False,
     page_index[used_pages] = np.arange(n_used, dtype=np.int32)
 
     is_i8 = cfg.kv_dtype == "i8"
+    is_fp8 = cfg.kv_dtype == "fp8"
     shape = (n_used, Hkv, PS, D)
-    if is_i8:
-        k_pages = np.full(shape, I8_POISON if poison else 0, dtype=np.int8)
-        v_pages = np.full(shape, I8_POISON if poison else 0, dtype=np.int8)
+    if is_i8 or is_fp8:
+        if is_i8:
+            k_pages = np.full(shape, I8_POISON if poison else 0, dtype=np.int8)
+            v_pages = np.full(shape, I8_POISON if poison else 0, dtype=np.int8)
+        else:
+            k_pages = np.full(shape, FP8_NAN if poison else 0, dtype=np.uint8)
+            v_pages = np.full(shape, FP8_NAN if poison else 0, dtype=np.uint8)
         sfill = np.float32(np.nan) if poison else np.float32(0)
         k_scale = np.full(shape[:3], sfill, dtype=np.float32)
         v_scale = np.full(shape[:3], sfill, dtype=np.float32)
@@ -166,6 +187,8 @@ def make_case(cfg: Config, seed: Optional[int] = None, poison: bool = False,
                                      (vf, v_pages, v_scale, logical_v)):
             if is_i8:
                 enc, sc = quantize_int8(src)
+            elif is_fp8:
+                enc, sc = quantize_fp8(src)
             else:
                 enc, sc = _to_bits(src, cfg.kv_dtype), None
             if keep is not None:

@@ -30,6 +30,10 @@ MUTANTS = {
     "f16_subnormal_exponent": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "f16_sign_lost": ("return sign ? -v : v;", "return v;"),
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "fp8_exponent_bias": ("v = ldexp((double)(m | 8), e - 10);", "v = ldexp((double)(m | 8), e - 11);"),
+    "fp8_subnormal_as_normal": ("v = ldexp((double)m, -9);", "v = ldexp((double)(m | 8), -10);"),
+    "fp8_scale_ignored": ("static int scaled_kv(int dtype) { return dtype == ORC_I8 || dtype == ORC_FP8; }",
+                          "static int scaled_kv(int dtype) { return dtype == ORC_I8; }"),
     "split_merge_missing_rescale": ("L += l[k] * exp(m[k] - M);", "L += l[k];"),
     "split_partition_max_wrong": ("m[k] = mk;", "m[k] = 0.0;"),
 }
@@ -37,11 +41,13 @@ MUTANTS = {
 PIN_SUITE = [
     lambda: pins.test_f16_decode_matches_numpy_all_patterns(oracle.lib()),
     lambda: pins.test_bf16_decode_matches_torch_all_patterns(oracle.lib()),
+    lambda: pins.test_fp8_e4m3_decode_matches_torch_all_patterns(oracle.lib()),
     *[(lambda s=s: pins.test_oracle_matches_pure_python_brute_force(s)) for s in pins.TINY_SHAPES],
     *[(lambda T=T: pins.test_split_merge_matches_unsplit(T)) for T in (16, 64)],
     pins.test_large_common_score_shift_is_harmless,
     pins.test_gqa_equals_mha_with_repeated_kv_heads_bitwise,
     pins.test_int8_with_unit_scales_equals_f16_of_same_integers,
+    pins.test_fp8_with_unit_scales_equals_f16_of_same_values,
 ]
 
 

@@ -22,6 +22,8 @@ TINY_SHAPES = [
     (8, 2, 64, "bf16", "bf16", 16, (15, 16, 17)),
     (4, 1, 64, "f16", "i8", 16, (33, 5)),
     (2, 2, 128, "bf16", "i8", 64, (64, 130)),
+    (4, 2, 64, "f16", "fp8", 16, (37, 20)),
+    (2, 1, 128, "bf16", "fp8", 64, (1, 70)),
 ]
 
 
@@ -42,6 +44,9 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float16).astype(np.float64)
     import torch
 
+    if dtype == "fp8":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.uint8)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
     return t.to(torch.float64).numpy()
 
@@ -50,6 +55,8 @@ def logical_floats(case, b, which):
     enc, sc = (case.logical_k if which == "k" else case.logical_v)[b]
     if case.cfg.kv_dtype == "i8":
         return enc.astype(np.float64) * sc.astype(np.float64)[..., None]
+    if case.cfg.kv_dtype == "fp8":
+        return decode_bits(enc, "fp8") * sc.astype(np.float64)[..., None]
     return decode_bits(enc, case.cfg.kv_dtype)
 
 
@@ -74,6 +81,30 @@ def test_bf16_decode_matches_torch_all_patterns(oracle_lib):
     nan = np.isnan(ref)
     assert (np.isnan(got) == nan).all()
     assert (got[~nan] == ref[~nan]).all()
+
+
+def test_fp8_e4m3_decode_matches_torch_all_patterns(oracle_lib):
+    bits = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    ref = decode_bits(bits, "fp8")
+    got = np.array([oracle_lib.oracle_fp8e4m3_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2                      # S.1111.111, both signs
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+
+
+def test_fp8_e4m3_closed_forms(oracle_lib):
+    """Values the OCP E4M3 definition fixes: 1.0, the largest finite value
+    (1.75 * 2^8), the smallest subnormal (2^-9), the largest subnormal, the
+    smallest normal (2^-6), negative zero; no infinities."""
+    f = oracle_lib.oracle_fp8e4m3_to_f64
+    assert f(0x38) == 1.0
+    assert f(0x7E) == 448.0 and f(0xFE) == -448.0
+    assert f(0x01) == 2.0 ** -9 and f(0x07) == 7 * 2.0 ** -9
+    assert f(0x08) == 2.0 ** -6
+    assert f(0x80) == 0.0 and math.copysign(1.0, f(0x80)) == -1.0
+    assert math.isnan(f(0x7F)) and math.isnan(f(0xFF))
+    assert all(math.isfinite(f(b)) for b in range(256) if b & 0x7F != 0x7F)
 
 
 # --------------------------------------------------------------------------
@@ -134,6 +165,19 @@ def test_int8_with_unit_scales_equals_f16_of_same_integers():
     c16 = tiny_case(4, 2, 64, "f16", "f16", 16, (37, 100), seed=7)
     c16.k_pages = c8.k_pages.astype(np.float16).view(np.uint16)
     c16.v_pages = c8.v_pages.astype(np.float16).view(np.uint16)
+    c16.q_bits = c8.q_bits
+    assert (oracle.paged_decode(c8) == oracle.paged_decode(c16)).all()
+
+
+def test_fp8_with_unit_scales_equals_f16_of_same_values():
+    """Every finite E4M3 value is exact in f16: fp8 codes with scale 1 give
+    the same fp64 inputs as f16 storage of the decoded values."""
+    c8 = tiny_case(4, 2, 64, "f16", "fp8", 16, (37, 100), seed=8)
+    c8.k_scale[:] = 1.0
+    c8.v_scale[:] = 1.0
+    c16 = tiny_case(4, 2, 64, "f16", "f16", 16, (37, 100), seed=8)
+    c16.k_pages = decode_bits(c8.k_pages, "fp8").astype(np.float16).view(np.uint16)
+    c16.v_pages = decode_bits(c8.v_pages, "fp8").astype(np.float16).view(np.uint16)
     c16.q_bits = c8.q_bits
     assert (oracle.paged_decode(c8) == oracle.paged_decode(c16)).all()
 
