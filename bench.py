@@ -219,7 +219,7 @@ def main():
         bt, lens = pool.block_tables(list(range(cfg.batch)), cfg.max_blocks)
     assert (bt == case.block_tables).all() and (lens == case.context_lens).all()
 
-    kv_bytes_layer = case.total_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * (1 if cfg.kv_dtype == "i8" else 2)
+    kv_bytes_layer = case.total_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * (1 if cfg.kv_dtype in ("i8", "fp8") else 2)
     rotate = args.rotate or max(1, -(-(1 << 30) // max(kv_bytes_layer, 1)))
     layers = [upload(case, "cuda") for _ in range(rotate)]
     q = layers[0].q
@@ -261,7 +261,7 @@ def main():
     got = out.to(torch.float64).cpu().numpy()
     ref = oracle.paged_decode(case)
     max_err = float(np.abs(got - ref).max())
-    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}[cfg.kv_dtype]
+    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}[cfg.kv_dtype]
 
     # W warm-up steps, then more (untimed) until the GPU has been busy for
     # WARMUP_SECONDS, so that clocks have settled before the timed region

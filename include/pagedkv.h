@@ -36,7 +36,7 @@
  *  - Layouts are dense, row-major, with no padding:
  *      q, out        [batch][num_q_heads][head_dim]
  *      k_pool/v_pool [num_pages][num_kv_heads][page_size][head_dim]
- *      k/v_scale     [num_pages][num_kv_heads][page_size]     (fp32, int8 only)
+ *      k/v_scale     [num_pages][num_kv_heads][page_size]     (fp32, int8 / fp8 only)
  *      block_tables  [batch][max_blocks]                      (int32)
  *      context_lens  [batch]                                  (int32)
  *    One page id addresses the same page in every layer's pools; block
@@ -70,8 +70,13 @@ typedef enum pkv_status {
 typedef enum pkv_dtype {
     PKV_F16 = 0,  /* IEEE binary16                                          */
     PKV_BF16 = 1, /* bfloat16                                               */
-    PKV_I8 = 2    /* symmetric int8 code; value = fp32 scale x code, one
+    PKV_I8 = 2,   /* symmetric int8 code; value = fp32 scale x code, one
                      scale per (page, kv head, slot), i.e. per token per head */
+    PKV_FP8_E4M3 = 3 /* OCP 8-bit float E4M3 ("e4m3fn": bias 7, no infinities,
+                     S.1111.111 = NaN, max 448); value = fp32 scale x code,
+                     scales laid out as for PKV_I8.  The FP8 KV cache of
+                     "TensorRT-LLM 推理加速实战", sections 8 and 8.1 (half the
+                     bytes of fp16 KV per token).                           */
 } pkv_dtype;
 
 int32_t pkv_abi_version(void);
@@ -153,7 +158,8 @@ pkv_status pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids,
 
 /* KV-cache bytes 2 x layers x kv_heads x head_dim x tokens x batch x bytes(dtype)
  * (section 8.1 of the engine-to-kernel-tuning page; the M_kv equation of the
- * aiqz.cc explainer).  int8 counts the codes only (scales excluded).
+ * aiqz.cc explainer).  int8 and fp8 count the codes only (scales excluded);
+ * fp8 is the page's 1-byte FP8 case.
  * Returns -1 for a negative argument or overflow. */
 int64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_t tokens,
                      int32_t batch, pkv_dtype dtype);
@@ -168,7 +174,7 @@ typedef struct pkv_decode_args {
     const void *k_pool;         /* device [num_pages][num_kv_heads][page_size][head_dim] */
     const void *v_pool;         /* device, same shape                                */
     const float *k_scale;       /* device [num_pages][num_kv_heads][page_size]; int8
-                                   KV only, otherwise NULL                           */
+                                   and fp8 KV only, otherwise NULL                   */
     const float *v_scale;
     const int32_t *block_tables;/* device [batch][max_blocks]; entry j of row b is the
                                    physical page of tokens [j*page_size, (j+1)*page_size)
@@ -205,12 +211,12 @@ typedef struct pkv_decode_args {
                                    (all sequences, all KV heads) are divided into this
                                    many equal contiguous shares, one per wave of a
                                    persistent grid.  0 = library default (4 waves per
-                                   compute unit for 16-bit KV, 8 for int8 KV);
+                                   compute unit, 8 for int8 KV);
                                    always capped at the number of tiles the batch
                                    can have.                                         */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16; out has the same type       */
     pkv_dtype kv_dtype;         /* PKV_F16 (with f16 q), PKV_BF16 (with bf16 q), or
-                                   PKV_I8 (with either)                              */
+                                   PKV_I8 or PKV_FP8_E4M3 (with either)              */
     float scale;                /* softmax scale applied to q.k (e.g. 1/sqrt(head_dim)) */
 } pkv_decode_args;
 
@@ -267,14 +273,14 @@ pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
 typedef struct pkv_write_args {
     const void *k_new;          /* device [n][num_kv_heads][head_dim], kv_dtype      */
     const void *v_new;
-    const float *k_scale_new;   /* device [n][num_kv_heads] fp32; int8 only, else NULL */
+    const float *k_scale_new;   /* device [n][num_kv_heads] fp32; int8 / fp8 only, else NULL */
     const float *v_scale_new;
     const int64_t *slots;       /* device [n]: page * page_size + offset, as returned by
                                    pkv_seq_alloc / pkv_append_tokens.  A slot outside
                                    [0, num_pages * page_size) is skipped.            */
     void *k_pool;               /* device pools, as in pkv_decode_args               */
     void *v_pool;
-    float *k_scale;             /* device pool scales; int8 only, else NULL          */
+    float *k_scale;             /* device pool scales; int8 / fp8 only, else NULL    */
     float *v_scale;
     int32_t n;                  /* tokens to write, >= 0                             */
     int32_t num_kv_heads;

@@ -22,8 +22,8 @@ PKV_ERR_UNSUPPORTED = -5
 PKV_ERR_WORKSPACE = -6
 PKV_ERR_DEVICE = -7
 
-PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2
-DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "i8": PKV_I8}
+PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "i8": PKV_I8, "fp8": PKV_FP8_E4M3}
 
 EXPORTED = [
     "pkv_abi_version", "pkv_status_string", "pkv_last_error", "pkv_device_count",

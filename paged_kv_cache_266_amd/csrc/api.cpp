@@ -66,7 +66,7 @@ static int32_t resolve_splits(const pkv_decode_args *a)
 {
     const int64_t tiles_per_seq = ((int64_t)a->max_context_len + kTileTokens - 1) / kTileTokens;
     const int64_t upper = std::max<int64_t>(1, (int64_t)a->batch * a->num_kv_heads * tiles_per_seq);
-    const int64_t per_cu = a->kv_dtype == PKV_I8 ? kDefaultWavesPerCU8 : kDefaultWavesPerCU16;
+    const int64_t per_cu = a->kv_dtype == PKV_I8 ? kDefaultWavesPerCUInt8 : kDefaultWavesPerCU;
     const int64_t want = a->num_splits > 0 ? a->num_splits : per_cu * device_cu_count();
     return (int32_t)std::min<int64_t>(std::min<int64_t>(want, upper), 1 << 24);
 }
@@ -145,20 +145,21 @@ static pkv_status validate(const pkv_decode_args *a, bool one_launch)
         return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len exceeds max_blocks * page_size");
     if (a->num_splits < 0)
         return fail(PKV_ERR_INVALID_ARG, "decode: num_splits must be >= 0");
-    bool kv_ok = (a->kv_dtype == PKV_I8 && (a->q_dtype == PKV_F16 || a->q_dtype == PKV_BF16)) ||
+    const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
+    bool kv_ok = (byte_kv && (a->q_dtype == PKV_F16 || a->q_dtype == PKV_BF16)) ||
                  (a->kv_dtype == PKV_F16 && a->q_dtype == PKV_F16) ||
                  (a->kv_dtype == PKV_BF16 && a->q_dtype == PKV_BF16);
     int group = a->num_q_heads / a->num_kv_heads;
     if (!kv_ok || !decode_instantiated(a->head_dim, a->page_size, group, a->q_dtype, a->kv_dtype))
         return fail(PKV_ERR_UNSUPPORTED,
                     "decode: supported set is head_dim {64,128}, page_size {16,64}, group {1,2,4,8}, "
-                    "(q,kv) in {(f16,f16),(bf16,bf16),(f16,i8),(bf16,i8)}");
+                    "(q,kv) in {(f16,f16),(bf16,bf16),(f16|bf16, i8|fp8)}");
     if (a->batch == 0)
         return PKV_OK;
     if (!a->q || !a->k_pool || !a->v_pool || !a->block_tables || !a->context_lens || !a->out)
         return fail(PKV_ERR_INVALID_ARG, "decode: null device pointer");
-    if (a->kv_dtype == PKV_I8 && (!a->k_scale || !a->v_scale))
-        return fail(PKV_ERR_INVALID_ARG, "decode: int8 KV needs k_scale and v_scale");
+    if (byte_kv && (!a->k_scale || !a->v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "decode: int8 / fp8 KV needs k_scale and v_scale");
     if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->out) ||
         ((uintptr_t)a->k_scale & 3u) || ((uintptr_t)a->v_scale & 3u) ||
         ((uintptr_t)a->block_tables & 3u) || ((uintptr_t)a->context_lens & 3u))
@@ -323,15 +324,16 @@ extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)
         return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: bad sizes");
     if (a->head_dim != 64 && a->head_dim != 128)
         return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: head_dim must be 64 or 128");
-    if (a->kv_dtype != PKV_F16 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_I8)
+    if (a->kv_dtype != PKV_F16 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_I8 &&
+        a->kv_dtype != PKV_FP8_E4M3)
         return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: unknown kv dtype");
     if (a->n == 0)
         return PKV_OK;
     if (!a->k_new || !a->v_new || !a->slots || !a->k_pool || !a->v_pool)
         return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: null device pointer");
-    bool i8 = a->kv_dtype == PKV_I8;
+    bool i8 = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;   // one scale per row
     if (i8 && (!a->k_scale_new || !a->v_scale_new || !a->k_scale || !a->v_scale))
-        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: int8 KV needs the four scale pointers");
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: int8 / fp8 KV needs the four scale pointers");
     if (!aligned16(a->k_new) || !aligned16(a->v_new) || !aligned16(a->k_pool) || !aligned16(a->v_pool) ||
         ((uintptr_t)a->slots & 7u))
         return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: K/V buffers must be 16-byte aligned, slots 8-byte");

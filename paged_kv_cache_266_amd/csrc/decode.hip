@@ -212,6 +212,16 @@ __device__ __forceinline__ float dot2(u32 k, u32 q, float acc)
                                       false);
 }
 
+// Two OCP E4M3 values (bytes 0, 1, or bytes 2, 3 of w) as floats; the
+// gfx950 converter decodes exactly this format (checked on the hardware
+// against the format definition for all 256 codes).
+template <bool HI>
+__device__ __forceinline__ float2 fp8_pair(u32 w)
+{
+    const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    return make_float2(v[0], v[1]);
+}
+
 // Unsigned byte e of w as float (v_cvt_f32_ubyteN).
 template <int E>
 __device__ __forceinline__ float ubyte(u32 w) { return (float)((w >> (8 * E)) & 0xFFu); }
@@ -293,7 +303,7 @@ __device__ __forceinline__ void store_coherent1(float *base, int bytes, int voff
 template <int D, int PS, int G, int QT, int KVT>
 struct Shape {
     static constexpr int PAGE = PS;                // tokens per page
-    static constexpr int EB = KVT == I8 ? 1 : 2;   // bytes per KV element
+    static constexpr int EB = KVT == I8 || KVT == FP8 ? 1 : 2;   // bytes per KV element
     static constexpr int ROW = D * EB;             // bytes per token row
     static constexpr int R = ROW / 16;             // lanes per token row
     static constexpr int LEVELS = R == 16 ? 4 : R == 8 ? 3 : 2;
@@ -558,8 +568,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 {
     using S = Shape<D, PS, G, QT, KVT>;
     constexpr int R = S::R, TPI = S::TPI, EPL = S::EPL, PPT = S::PPT, LEVELS = S::LEVELS;
+    // byte KV (int8 or fp8): one fp32 scale per token, q kept as fp32
+    constexpr bool kByte = KVT == I8 || KVT == FP8;
     constexpr bool kI8 = KVT == I8;
-    constexpr int QW = kI8 ? 8 : 4;   // dwords of q per head per lane
+    constexpr int QW = kByte ? 8 : 4;   // dwords of q per head per lane
 
     __shared__ float s_p[S::PSTRIDE];
 
@@ -655,11 +667,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 my_phys = ph[pg];
         return my_phys;
     };
-    // K and V scales of this lane's own token of the cursor's tile (int8).
+    // K and V scales of this lane's own token of the cursor's tile (byte KV).
     auto own_scales = [&](const Cursor &c, const int (&ph)[PPT], float &ks, float &vs) {
         ks = 1.0f;
         vs = 1.0f;
-        if constexpr (kI8) {
+        if constexpr (kByte) {
             const int my_phys = own_page(ph);
             const bool ok = my_phys >= 0 && c.k * kTileTokens + TPI * j + r < c.n;
             const size_t si = ok ? ((size_t)my_phys * Hkv + c.g) * PS + (TPI * j) % PS + r : 0;
@@ -686,14 +698,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     };
 
     // q in the form the dot products use: packed pairs (16-bit KV) or fp32
-    // values with the -128 * sum(q) bias of the unsigned-byte trick (int8).
+    // values (byte KV), for int8 with the -128 * sum(q) bias of the
+    // unsigned-byte trick.
     u32 qw[G][4];
-    float qf[kI8 ? G : 1][kI8 ? 16 : 1];
+    float qf[kByte ? G : 1][kByte ? 16 : 1];
     float qbias[G];
     auto set_q = [&](const u32 (&raw)[G][QW]) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if constexpr (!kI8) {
+            if constexpr (!kByte) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     qw[h][v] = raw[h][v];
@@ -706,7 +719,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     qf[h][2 * e + 1] = q_hi<QT>(raw[h][e]);
                     s += qf[h][2 * e] + qf[h][2 * e + 1];
                 }
-                qbias[h] = -128.0f * s;
+                qbias[h] = kI8 ? -128.0f * s : 0.0f;
             }
         }
     };
@@ -739,7 +752,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         (std::make_integer_sequence<int, R>{});
     // int8 KV: the next segment's raw q is fetched a tile ahead (its fp32
     // form takes longer to set up)
-    u32 qraw[kI8 ? G : 1][QW];
+    u32 qraw[kByte ? G : 1][QW];
     {
         u32 q0[G][QW];
         load_q(cur, q0);
@@ -771,7 +784,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
             for (int pg = 0; pg < PPT; ++pg)
                 ph_nxt[pg] = -1;
-        if constexpr (kI8) {
+        if constexpr (kByte) {
             if (seg_end && !last_in_range)
                 load_q(nxt, qraw);
         }
@@ -786,11 +799,23 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                  for (int h = 0; h < G; ++h) {
                      float a;
-                     if constexpr (!kI8) {
+                     if constexpr (!kByte) {
                          a = dot2<KVT>(kc.x, qw[h][0], 0.0f);
                          a = dot2<KVT>(kc.y, qw[h][1], a);
                          a = dot2<KVT>(kc.z, qw[h][2], a);
                          a = dot2<KVT>(kc.w, qw[h][3], a);
+                     } else if constexpr (KVT == FP8) {
+                         // E4M3 pairs through the hardware converter
+                         const u32 wd[4] = {kc.x, kc.y, kc.z, kc.w};
+                         a = 0.0f;
+#pragma unroll
+                         for (int q4 = 0; q4 < 4; ++q4) {
+                             const float2 lo = fp8_pair<false>(wd[q4]), hi = fp8_pair<true>(wd[q4]);
+                             a = fmaf(qf[h][4 * q4 + 0], lo.x, a);
+                             a = fmaf(qf[h][4 * q4 + 1], lo.y, a);
+                             a = fmaf(qf[h][4 * q4 + 2], hi.x, a);
+                             a = fmaf(qf[h][4 * q4 + 3], hi.y, a);
+                         }
                      } else {
                          // code + 128 as unsigned bytes; the -128 * sum(q) bias restores the sign
                          const u32 wd[4] = {kc.x ^ 0x80808080u, kc.y ^ 0x80808080u, kc.z ^ 0x80808080u,
@@ -857,7 +882,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                  ring[I] = ka.template load<I>(lane_off);
                  float vf[EPL];
                  const u32 wv[4] = {vc.x, vc.y, vc.z, vc.w};
-                 if constexpr (kI8) {
+                 if constexpr (KVT == FP8) {
+#pragma unroll
+                     for (int q4 = 0; q4 < 4; ++q4) {
+                         const float2 lo = fp8_pair<false>(wv[q4]), hi = fp8_pair<true>(wv[q4]);
+                         vf[4 * q4 + 0] = lo.x;
+                         vf[4 * q4 + 1] = lo.y;
+                         vf[4 * q4 + 2] = hi.x;
+                         vf[4 * q4 + 3] = hi.y;
+                     }
+                 } else if constexpr (kI8) {
 #pragma unroll
                      for (int q4 = 0; q4 < 4; ++q4) {
                          const u32 u = wv[q4] ^ 0x80808080u;
@@ -947,7 +981,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             any_bad = false;
             piece_from_start = true;
             if (!last_in_range) {
-                if constexpr (kI8) {
+                if constexpr (kByte) {
                     set_q(qraw);   // loaded a tile ahead
                 } else {
                     // the next segment's q: loaded now, behind the next
@@ -1136,6 +1170,8 @@ int launch_dtype(const DecodeParams &p, int qt, int kvt, hipStream_t s)
     if (qt == BF16 && kvt == BF16) return launch_one<D, PS, G, BF16, BF16>(p, s);
     if (qt == F16 && kvt == I8) return launch_one<D, PS, G, F16, I8>(p, s);
     if (qt == BF16 && kvt == I8) return launch_one<D, PS, G, BF16, I8>(p, s);
+    if (qt == F16 && kvt == FP8) return launch_one<D, PS, G, F16, FP8>(p, s);
+    if (qt == BF16 && kvt == FP8) return launch_one<D, PS, G, BF16, FP8>(p, s);
     return (int)hipErrorInvalidValue;
 }
 
@@ -1156,7 +1192,7 @@ int launch_group(const DecodeParams &p, int G, int qt, int kvt, hipStream_t s)
 bool decode_instantiated(int D, int PS, int G, int qt, int kvt)
 {
     bool pair = (qt == F16 && kvt == F16) || (qt == BF16 && kvt == BF16) ||
-                ((qt == F16 || qt == BF16) && kvt == I8);
+                ((qt == F16 || qt == BF16) && (kvt == I8 || kvt == FP8));
     return (D == 64 || D == 128) && (PS == 16 || PS == 64) && (G == 1 || G == 2 || G == 4 || G == 8) &&
            pair;
 }

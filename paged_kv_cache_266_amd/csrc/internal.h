@@ -18,14 +18,14 @@ pkv_status fail(pkv_status code, const char *msg);
 // Tokens per wave-iteration of the decode kernel.
 constexpr int kTileTokens = 64;
 // Default waves per compute unit of the persistent grid (measured on
-// MI355X): one per SIMD for 16-bit KV, where a second co-resident wave on a
-// SIMD only slows the first (and the grid ends on the slower one); two per
-// SIMD for int8 KV, whose conversions leave more arithmetic to overlap with
-// memory latency.
-constexpr int kDefaultWavesPerCU16 = 4;
-constexpr int kDefaultWavesPerCU8 = 8;
+// MI355X): one per SIMD for 16-bit and fp8 KV, where a second co-resident
+// wave on a SIMD only slows the first (and the grid ends on the slower
+// one); two per SIMD for int8 KV, whose sign trick and conversions leave
+// more arithmetic to overlap with memory latency.
+constexpr int kDefaultWavesPerCU = 4;
+constexpr int kDefaultWavesPerCUInt8 = 8;
 
-enum DType : int { F16 = 0, BF16 = 1, I8 = 2 };
+enum DType : int { F16 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
 
 // Everything the decode kernels read; built by the host from pkv_decode_args.
 struct DecodeParams {

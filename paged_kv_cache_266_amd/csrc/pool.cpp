@@ -226,7 +226,8 @@ extern "C" int64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_d
     switch (dtype) {
     case PKV_F16:
     case PKV_BF16: e = 2; break;
-    case PKV_I8: e = 1; break;
+    case PKV_I8:
+    case PKV_FP8_E4M3: e = 1; break;
     default: return -1;
     }
     if (layers < 0 || kv_heads < 0 || head_dim < 0 || tokens < 0 || batch < 0)

@@ -16,7 +16,7 @@ from ._lib import DTYPE_CODES, DecodeArgs, WriteArgs, check, lib
 def _dtype_name(t) -> str:
     import torch
 
-    m = {torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+    m = {torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8", torch.float8_e4m3fn: "fp8"}
     if t.dtype not in m:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return m[t.dtype]
@@ -123,7 +123,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     """Single-token decode attention over a paged KV cache.
 
     q [B][Hq][D] f16/bf16; k_pool, v_pool [num_pages][Hkv][PS][D] of the same
-    type as q or int8 (then k_scale, v_scale [num_pages][Hkv][PS] fp32);
+    type as q, or int8 / float8_e4m3fn (then k_scale, v_scale
+    [num_pages][Hkv][PS] fp32);
     block_tables [B][max_blocks] int32; context_lens [B] int32 (device).
     ``max_context_len`` is a host-side bound on context_lens.  ``num_splits``
     is the number of waves sharing the batch's tiles (0 = library default).

@@ -21,6 +21,10 @@ real model or dataset.
                          per KV head, 16-token pages (the vLLM block size the
                          same section 8 compares against), 256 sequences with
                          lognormal lengths (median 512, clipped to [1, 4096]).
+* ``llama3_8b_gqa_fp8`` -- the Llama-3-8B GQA workload with its K/V stored as
+                         FP8 E4M3 with one fp32 scale per token per KV head
+                         (the FP8 KV cache of "TensorRT-LLM 推理加速实战",
+                         section 8).
 
 Where the workload statement leaves a value open (pool sizes of the last three
 configs, the lognormal sigma, the softmax scale) the plainest reading is used:
@@ -84,6 +88,9 @@ CONFIGS: Dict[str, Config] = {
                "fixed", (131072, 131072, 131072, 131072)),
         Config("qwen_1p8b_int8", 256, 16, 16, 128, "f16", "i8", 16, 32768, 2665,
                "lognormal", (512, 1.0, 1, 4096)),
+        # the GQA workload with an FP8 (E4M3) KV cache
+        Config("llama3_8b_gqa_fp8", 64, 32, 8, 128, "bf16", "fp8", 64, 16384, 2666,
+               "uniform", (512, 4096)),
     ]
 }
 

@@ -9,8 +9,11 @@ import oracle
 from synth import get_config, make_case
 from synth.device import upload
 
-# max-abs tolerances on outputs, by KV storage type
-TOL = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2}
+# max-abs tolerances on outputs, by KV storage type.  fp8 has no stated
+# tolerance: its codes decode exactly (as int8 codes do), the arithmetic is
+# the int8 path's fp32 accumulation, and the output rounding is the q type's,
+# so the bf16 bound is used.
+TOL = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}
 
 
 def note(msg):

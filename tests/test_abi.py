@@ -65,6 +65,9 @@ def validate(a):
 def test_valid_arguments_pass_validation():
     assert validate(good_args()) == 0
     assert validate(good_args(kv_dtype=_lib.PKV_I8, k_scale=FAKE, v_scale=FAKE)) == 0
+    assert validate(good_args(kv_dtype=_lib.PKV_FP8_E4M3, k_scale=FAKE, v_scale=FAKE)) == 0
+    assert validate(good_args(q_dtype=_lib.PKV_F16, kv_dtype=_lib.PKV_FP8_E4M3, k_scale=FAKE,
+                              v_scale=FAKE)) == 0
     assert validate(good_args(q_dtype=_lib.PKV_F16, kv_dtype=_lib.PKV_F16)) == 0
     assert validate(good_args(batch=0, q=None)) == 0
 
@@ -76,6 +79,8 @@ def test_valid_arguments_pass_validation():
     (dict(page_size=32, max_blocks=128), _lib.PKV_ERR_UNSUPPORTED),
     (dict(q_dtype=_lib.PKV_F16), _lib.PKV_ERR_UNSUPPORTED),      # f16 q with bf16 KV
     (dict(kv_dtype=_lib.PKV_I8), _lib.PKV_ERR_INVALID_ARG),      # int8 without scales
+    (dict(kv_dtype=_lib.PKV_FP8_E4M3), _lib.PKV_ERR_INVALID_ARG),  # fp8 without scales
+    (dict(kv_dtype=4), _lib.PKV_ERR_UNSUPPORTED),                # no such type
     (dict(q=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(out=FAKE + 8), _lib.PKV_ERR_INVALID_ARG),              # misaligned
     (dict(max_context_len=4097), _lib.PKV_ERR_INVALID_ARG),      # > max_blocks * page_size
@@ -160,6 +165,7 @@ def test_launch_without_a_device_reports_device_error():
 def test_kv_bytes_helper():
     assert pkv.kv_bytes(80, 8, 128, 1, 1, "bf16") == 327680
     assert pkv.kv_bytes(80, 8, 128, 1, 1, "i8") == 163840
+    assert pkv.kv_bytes(80, 8, 128, 1, 1, "fp8") == 163840   # the page's FP8 figure
     assert pkv.kv_bytes(1, 8, 128, 131072, 4, "bf16") == 2_147_483_648
     assert _lib.lib().pkv_kv_bytes(-1, 8, 128, 1, 1, 1) == -1
     assert _lib.lib().pkv_kv_bytes(1 << 30, 1 << 30, 1 << 30, 1 << 40, 1, 1) == -1  # overflow

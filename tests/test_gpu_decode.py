@@ -35,7 +35,7 @@ def _gpu():
 # The five workloads at full size, in the launch configuration the benchmark
 # times (default partition length), compared on every output element.
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", ORDER + ["llama3_8b_gqa_fp8"])
 def test_parity_full_config(name):
     cfg = CONFIGS[name]
     note(f"[parity] {name}: B={cfg.batch} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} "
@@ -53,7 +53,8 @@ def test_parity_full_config(name):
 
 SUPPORTED = [(D, PS, G, qd, kvd)
              for D, PS, G in itertools.product((64, 128), (16, 64), (1, 2, 4, 8))
-             for qd, kvd in (("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"))]
+             for qd, kvd in (("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"),
+                             ("f16", "fp8"), ("bf16", "fp8"))]
 
 
 @pytest.mark.parametrize("D,PS,G,qd,kvd", SUPPORTED)

@@ -40,6 +40,8 @@ def _as_torch(a, dtype_name, device):
 
     if dtype_name == "i8":
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    if dtype_name == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device).view(torch.float8_e4m3fn)
     t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
     return t.view(torch_dtype(dtype_name)).to(device)
 
@@ -49,6 +51,8 @@ def _as_torch(a, dtype_name, device):
     (32, 8, 128, "bf16", "bf16", 64, (300, 64, 1, 129)),
     (16, 16, 128, "f16", "i8", 16, (77, 200, 33)),
     (8, 4, 128, "bf16", "i8", 64, (65, 130)),
+    (16, 4, 128, "bf16", "fp8", 64, (200, 64, 3)),
+    (8, 8, 64, "f16", "fp8", 16, (40, 17)),
 ])
 def test_append_write_then_decode(Hq, Hkv, D, qd, kvd, PS, lens):
     import torch
@@ -61,12 +65,12 @@ def test_append_write_then_decode(Hq, Hkv, D, qd, kvd, PS, lens):
     dev = "cuda"
     shape = (cfg.num_pages, Hkv, PS, D)
     kv_t = torch_dtype(kvd)
-    k_pool = torch.zeros(shape, dtype=kv_t, device=dev)
-    v_pool = torch.zeros(shape, dtype=kv_t, device=dev)
-    i8 = kvd == "i8"
+    i8 = kvd in ("i8", "fp8")            # byte codes with one scale per row
+    k_pool = torch.zeros(shape, dtype=torch.uint8 if kvd == "fp8" else kv_t, device=dev).view(kv_t)
+    v_pool = torch.zeros(shape, dtype=torch.uint8 if kvd == "fp8" else kv_t, device=dev).view(kv_t)
     k_sc = torch.zeros(shape[:3], dtype=torch.float32, device=dev) if i8 else None
     v_sc = torch.zeros(shape[:3], dtype=torch.float32, device=dev) if i8 else None
-    host_k = np.zeros(shape, dtype=np.int8 if i8 else np.uint16)
+    host_k = np.zeros(shape, dtype=(np.uint8 if kvd == "fp8" else np.int8) if i8 else np.uint16)
     host_v = np.zeros_like(host_k)
     host_ks = np.zeros(shape[:3], dtype=np.float32) if i8 else None
     host_vs = np.zeros_like(host_ks) if i8 else None
@@ -101,8 +105,8 @@ def test_append_write_then_decode(Hq, Hkv, D, qd, kvd, PS, lens):
     torch.cuda.synchronize()
 
     # the device pools hold exactly the bytes the host scatter put there
-    assert np.array_equal(k_pool.cpu().view(torch.int8 if i8 else torch.int16).numpy().view(host_k.dtype), host_k)
-    assert np.array_equal(v_pool.cpu().view(torch.int8 if i8 else torch.int16).numpy().view(host_v.dtype), host_v)
+    assert np.array_equal(k_pool.cpu().view(torch.uint8 if i8 else torch.int16).numpy().view(host_k.dtype), host_k)
+    assert np.array_equal(v_pool.cpu().view(torch.uint8 if i8 else torch.int16).numpy().view(host_v.dtype), host_v)
     if i8:
         assert np.array_equal(k_sc.cpu().numpy(), host_ks)
         assert np.array_equal(v_sc.cpu().numpy(), host_vs)
