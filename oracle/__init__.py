@@ -65,6 +65,11 @@ def load(path: str):
     L.oracle_scatter_rows.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint8)]
     L.oracle_scatter_rows.restype = ci
+    L.oracle_fp8e4m3_encode.argtypes = [ctypes.c_float]
+    L.oracle_fp8e4m3_encode.restype = ctypes.c_uint8
+    L.oracle_quantize_rows.argtypes = [ci, ci, ci, ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
+    L.oracle_quantize_rows.restype = ci
     return L
 
 
@@ -181,6 +186,25 @@ def scatter_rows(pool: np.ndarray, slots: np.ndarray, src: np.ndarray) -> None:
                                    _ptr(pool_b, ctypes.c_uint8))
     if rc != 0:
         raise OracleError(f"oracle_scatter_rows returned {rc}")
+
+
+def quantize_rows(x: np.ndarray, kind: str):
+    """Per-row int8 / fp8 encoding of ``x [..., D]`` (float32): returns
+    (codes with x's leading shape, int8 or uint8; scales float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    n = x.size // D
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    rc = lib().oracle_quantize_rows(n, D, DTYPE_CODE[kind], _ptr(x, ctypes.c_float),
+                                    _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_float))
+    if rc != 0:
+        raise OracleError(f"oracle_quantize_rows returned {rc}")
+    return (codes.view(np.int8) if kind == "i8" else codes), scales
+
+
+def fp8e4m3_encode(y: float) -> int:
+    return int(lib().oracle_fp8e4m3_encode(y))
 
 
 def f16_to_f64(bits: int) -> float:

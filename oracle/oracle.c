@@ -376,3 +376,69 @@ int oracle_scatter_rows(int n, int Hkv, int PS, int num_pages, int row_bytes,
     }
     return ORC_OK;
 }
+
+/*
+ * Quantisation of appended K/V rows, the encodings the readings fix for the
+ * pages' int8 and FP8 KV caches: per row (one token of one KV head) of D
+ * values, in fp32 arithmetic,
+ *     s    = max(max_d |x_d|, 1e-5) / Q        (Q = 127 for int8, 448 for fp8)
+ *     code = round-half-to-even(x_d / s)        (int8: clipped to [-127, 127];
+ *                                                fp8: the nearest E4M3 value)
+ * Codes are written as bytes ([n][D]), scales as fp32 ([n]).
+ */
+
+/* Nearest OCP E4M3 code to y, ties to even; magnitudes that round above
+ * the largest finite value (448) give 448. */
+uint8_t oracle_fp8e4m3_encode(float y)
+{
+    if (y != y)
+        return 0x7f;
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    double a = fabs((double)y);
+    if (a >= 464.0)                    /* at or past the midpoint above 448 */
+        return sign | 0x7e;
+    if (a < ldexp(1.0, -6)) {          /* subnormal range: multiples of 2^-9 */
+        double m = rint(a * 512.0);    /* exact product; rint ties to even */
+        return sign | (uint8_t)m;      /* m == 8 is the smallest normal, code 0x08 */
+    }
+    int e;
+    frexp(a, &e);                      /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                            /* a = 1.x * 2^e */
+    double m = rint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8.0) {
+        m = 0.0;
+        e += 1;
+    }
+    int field = e + 7;
+    if (field > 15 || (field == 15 && m == 7.0))
+        return sign | 0x7e;
+    return sign | (uint8_t)((field << 3) | (int)m);
+}
+
+int oracle_quantize_rows(int n, int D, int kind, const float *x, uint8_t *codes, float *scales)
+{
+    if (n < 0 || D <= 0 || (kind != ORC_I8 && kind != ORC_FP8))
+        return ORC_BAD_ARG;
+    const float qmax = kind == ORC_I8 ? 127.0f : 448.0f;
+    for (int i = 0; i < n; ++i) {
+        const float *row = x + (size_t)i * D;
+        float amax = 0.0f;
+        for (int d = 0; d < D; ++d)
+            amax = fmaxf(amax, fabsf(row[d]));
+        const float s = fmaxf(amax, 1e-5f) / qmax;
+        scales[i] = s;
+        for (int d = 0; d < D; ++d) {
+            const float y = row[d] / s;
+            uint8_t c;
+            if (kind == ORC_I8) {
+                float r = rintf(y);
+                r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+                c = (uint8_t)(int8_t)r;
+            } else {
+                c = oracle_fp8e4m3_encode(y);
+            }
+            codes[(size_t)i * D + d] = c;
+        }
+    }
+    return ORC_OK;
+}

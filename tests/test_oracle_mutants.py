@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_quant as quant
 
 MUTANTS = {
     "interleaved_gqa_groups": ("int g = h / (p->Hq / p->Hkv);", "int g = h % p->Hkv;"),
@@ -32,6 +33,12 @@ MUTANTS = {
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     "fp8_exponent_bias": ("v = ldexp((double)(m | 8), e - 10);", "v = ldexp((double)(m | 8), e - 11);"),
     "fp8_subnormal_as_normal": ("v = ldexp((double)m, -9);", "v = ldexp((double)(m | 8), -10);"),
+    "quant_int8_range": ("const float qmax = kind == ORC_I8 ? 127.0f : 448.0f;",
+                         "const float qmax = kind == ORC_I8 ? 128.0f : 448.0f;"),
+    "quant_truncates": ("float r = rintf(y);", "float r = truncf(y);"),
+    "fp8_encode_mantissa_floor": ("double m = rint((ldexp(a, -e) - 1.0) * 8.0);",
+                                  "double m = floor((ldexp(a, -e) - 1.0) * 8.0);"),
+    "fp8_encode_no_carry": ("        m = 0.0;\n        e += 1;", "        m = 7.0;"),
     "fp8_scale_ignored": ("static int scaled_kv(int dtype) { return dtype == ORC_I8 || dtype == ORC_FP8; }",
                           "static int scaled_kv(int dtype) { return dtype == ORC_I8; }"),
     "split_merge_missing_rescale": ("L += l[k] * exp(m[k] - M);", "L += l[k];"),
@@ -48,6 +55,11 @@ PIN_SUITE = [
     pins.test_gqa_equals_mha_with_repeated_kv_heads_bitwise,
     pins.test_int8_with_unit_scales_equals_f16_of_same_integers,
     pins.test_fp8_with_unit_scales_equals_f16_of_same_values,
+    lambda: quant.test_quantiser_matches_generator_encoders("i8"),
+    lambda: quant.test_quantiser_matches_generator_encoders("fp8"),
+    quant.test_int8_ties_round_to_even,
+    quant.test_fp8_encode_round_trips_every_finite_code,
+    quant.test_fp8_encode_ties_and_saturation,
 ]
 
 
