@@ -271,9 +271,11 @@ pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
  * ===================================================================== */
 
 typedef struct pkv_write_args {
-    const void *k_new;          /* device [n][num_kv_heads][head_dim], kv_dtype      */
+    const void *k_new;          /* device [n][num_kv_heads][head_dim], src_dtype     */
     const void *v_new;
-    const float *k_scale_new;   /* device [n][num_kv_heads] fp32; int8 / fp8 only, else NULL */
+    const float *k_scale_new;   /* device [n][num_kv_heads] fp32: the scales of
+                                   already-encoded int8 / fp8 rows (src_dtype ==
+                                   kv_dtype); NULL otherwise                         */
     const float *v_scale_new;
     const int64_t *slots;       /* device [n]: page * page_size + offset, as returned by
                                    pkv_seq_alloc / pkv_append_tokens.  A slot outside
@@ -287,9 +289,20 @@ typedef struct pkv_write_args {
     int32_t head_dim;           /* 64 or 128                                        */
     int32_t page_size;
     int32_t num_pages;
-    pkv_dtype kv_dtype;
+    pkv_dtype kv_dtype;         /* type of the pools                                 */
+    pkv_dtype src_dtype;        /* type of k_new / v_new: kv_dtype (rows are copied
+                                   as they are), or PKV_F16 / PKV_BF16 with an int8
+                                   or fp8 pool: each row (one token, one KV head) is
+                                   quantised on the device, s = max(max|x|, 1e-5) /
+                                   Q in fp32 (Q = 127 int8, 448 fp8), codes rounded
+                                   half to even (int8 clipped to +-127, fp8 the
+                                   nearest E4M3 value, saturating at 448), and s is
+                                   stored in k_scale / v_scale                       */
 } pkv_write_args;
 
+/* Writes the n new tokens' K and V (all KV heads) at their slots; for an
+ * int8 / fp8 pool fed f16 / bf16 rows, quantises them first (see src_dtype).
+ * Asynchronous on `stream`.  Slots must be distinct. */
 pkv_status pkv_write_kv(const pkv_write_args *args, void *stream);
 
 #ifdef __cplusplus

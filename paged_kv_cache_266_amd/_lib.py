@@ -68,6 +68,7 @@ class WriteArgs(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("n", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+        ("src_dtype", ctypes.c_int),
     ]
 
 

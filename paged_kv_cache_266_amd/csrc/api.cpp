@@ -327,31 +327,39 @@ extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)
     if (a->kv_dtype != PKV_F16 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_I8 &&
         a->kv_dtype != PKV_FP8_E4M3)
         return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: unknown kv dtype");
+    const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;   // one scale per row
+    const bool quantise = byte_kv && (a->src_dtype == PKV_F16 || a->src_dtype == PKV_BF16);
+    if (a->src_dtype != a->kv_dtype && !quantise)
+        return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: src_dtype must equal kv_dtype, or be f16 / bf16 "
+                                         "with an int8 / fp8 pool");
     if (a->n == 0)
         return PKV_OK;
     if (!a->k_new || !a->v_new || !a->slots || !a->k_pool || !a->v_pool)
         return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: null device pointer");
-    bool i8 = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;   // one scale per row
-    if (i8 && (!a->k_scale_new || !a->v_scale_new || !a->k_scale || !a->v_scale))
-        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: int8 / fp8 KV needs the four scale pointers");
+    if (byte_kv && (!a->k_scale || !a->v_scale || (!quantise && (!a->k_scale_new || !a->v_scale_new))))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: int8 / fp8 KV needs the pool scales (and, for "
+                                         "encoded rows, their scales)");
     if (!aligned16(a->k_new) || !aligned16(a->v_new) || !aligned16(a->k_pool) || !aligned16(a->v_pool) ||
         ((uintptr_t)a->slots & 7u))
         return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: K/V buffers must be 16-byte aligned, slots 8-byte");
     WriteParams p{};
     p.k_new = a->k_new;
     p.v_new = a->v_new;
-    p.k_scale_new = i8 ? a->k_scale_new : nullptr;
-    p.v_scale_new = i8 ? a->v_scale_new : nullptr;
+    p.k_scale_new = byte_kv && !quantise ? a->k_scale_new : nullptr;
+    p.v_scale_new = byte_kv && !quantise ? a->v_scale_new : nullptr;
     p.slots = a->slots;
     p.k_pool = a->k_pool;
     p.v_pool = a->v_pool;
-    p.k_scale = i8 ? a->k_scale : nullptr;
-    p.v_scale = i8 ? a->v_scale : nullptr;
+    p.k_scale = byte_kv ? a->k_scale : nullptr;
+    p.v_scale = byte_kv ? a->v_scale : nullptr;
     p.n = a->n;
     p.num_kv_heads = a->num_kv_heads;
     p.page_size = a->page_size;
     p.num_pages = a->num_pages;
-    p.row_bytes = a->head_dim * (i8 ? 1 : 2);
+    p.row_bytes = a->head_dim * (byte_kv ? 1 : 2);
+    p.head_dim = a->head_dim;
+    p.src_dtype = a->src_dtype;
+    p.kv_dtype = a->kv_dtype;
     int err = launch_write_kv(p, stream);
     return err ? device_fail(err, "pkv_write_kv") : PKV_OK;
 }

@@ -1152,6 +1152,69 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteParams p)
     }
 }
 
+// ---- quantise-on-append ------------------------------------------------------
+//
+// One wave per appended row (one token of one KV head) of f16 / bf16 values
+// into an int8 or fp8 pool: the row's exact max magnitude (wave reduction),
+// s = max(amax, 1e-5) / Q in fp32 (Q = 127 for int8, 448 for E4M3), then
+// each value's code: round-half-to-even of x / s (int8 clipped to +-127;
+// fp8 through the hardware converter, which rounds to nearest even; |x / s|
+// never exceeds 448 by more than the rounding of s, which still rounds to
+// 448).  The scale goes to the pool's scale array at the row's slot.
+
+template <int D, int SRC, int KVT>
+__global__ __launch_bounds__(64) void write_kv_quant_kernel(WriteParams p)
+{
+    constexpr int EPL = D / 64;   // values per lane
+    constexpr float kQ = KVT == I8 ? 127.0f : 448.0f;
+    const int lane = threadIdx.x;
+    const size_t rows = (size_t)p.n * p.num_kv_heads;
+    for (size_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const size_t i = row / p.num_kv_heads;
+        const int g = (int)(row % p.num_kv_heads);
+        const int64_t slot = p.slots[i];
+        if (slot < 0 || slot >= (int64_t)p.num_pages * p.page_size)
+            continue;
+        const int64_t page = slot / p.page_size, off = slot % p.page_size;
+        const size_t dst_row = ((size_t)page * p.num_kv_heads + g) * p.page_size + off;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(which ? p.v_new : p.k_new) + row * D + EPL * lane;
+            float x[EPL];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const u32 bits = src[e];
+                x[e] = SRC == BF16 ? __builtin_bit_cast(float, bits << 16)
+                                   : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+                amax = fmaxf(amax, fabsf(x[e]));
+            }
+            amax = wave_max(amax);
+            const float s = fmaxf(amax, 1e-5f) / kQ;
+            uint8_t code[EPL];
+            if constexpr (KVT == I8) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float r = fminf(fmaxf(rintf(x[e] / s), -127.0f), 127.0f);
+                    code[e] = (uint8_t)(int8_t)r;
+                }
+            } else {
+                const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, EPL > 1 ? x[EPL - 1] / s : 0.0f, 0, false);
+                code[0] = (uint8_t)(packed & 0xff);
+                if constexpr (EPL > 1)
+                    code[EPL - 1] = (uint8_t)((packed >> 8) & 0xff);
+            }
+            uint8_t *dst = reinterpret_cast<uint8_t *>(which ? p.v_pool : p.k_pool) + dst_row * D + EPL * lane;
+            if constexpr (EPL == 2)
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(code[0] | (code[1] << 8));
+            else
+                dst[0] = code[0];
+            if (lane == 0)
+                (which ? p.v_scale : p.k_scale)[dst_row] = s;
+        }
+    }
+}
+
 // ---- dispatch -------------------------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -1220,8 +1283,25 @@ int launch_splitk_reduce(const DecodeParams &p, int D, int qt, void *stream)
                                 (hipStream_t)stream);
 }
 
+template <int D, int SRC>
+static int launch_quant(const WriteParams &p, hipStream_t s)
+{
+    const size_t rows = (size_t)p.n * p.num_kv_heads;
+    const unsigned blocks = (unsigned)(rows < 65535 ? rows : 65535);
+    void *args[] = {const_cast<WriteParams *>(&p)};
+    const void *fn = p.kv_dtype == I8 ? (const void *)&write_kv_quant_kernel<D, SRC, I8>
+                                      : (const void *)&write_kv_quant_kernel<D, SRC, FP8>;
+    return (int)hipLaunchKernel(fn, dim3(blocks), dim3(64), args, 0, s);
+}
+
 int launch_write_kv(const WriteParams &p, void *stream)
 {
+    if (p.src_dtype != p.kv_dtype) {   // f16 / bf16 rows into an int8 / fp8 pool
+        hipStream_t s = (hipStream_t)stream;
+        if (p.head_dim == 64)
+            return p.src_dtype == BF16 ? launch_quant<64, BF16>(p, s) : launch_quant<64, F16>(p, s);
+        return p.src_dtype == BF16 ? launch_quant<128, BF16>(p, s) : launch_quant<128, F16>(p, s);
+    }
     const size_t total = (size_t)p.n * p.num_kv_heads * (p.row_bytes / 16);
     size_t blocks = (total + 255) / 256;
     if (blocks > 65535)

@@ -68,7 +68,10 @@ struct WriteParams {
     int32_t num_kv_heads;
     int32_t page_size;
     int32_t num_pages;
-    int32_t row_bytes;
+    int32_t row_bytes;    // bytes of one pool row (one token, one KV head)
+    int32_t head_dim;
+    int32_t src_dtype;    // type of k_new / v_new
+    int32_t kv_dtype;     // type of the pools
 };
 
 // Kernel launchers (device code lives in the .hip translation units).

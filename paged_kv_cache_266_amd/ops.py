@@ -154,7 +154,12 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
 
 def write_kv(k_new, v_new, slots, k_pool, v_pool, *, k_scale_new=None, v_scale_new=None,
              k_scale=None, v_scale=None, stream=None) -> None:
-    """Scatter appended tokens' K/V ([n][Hkv][D]) into their pool slots."""
+    """Scatter appended tokens' K/V ([n][Hkv][D]) into their pool slots.
+
+    With an int8 / fp8 pool, k_new / v_new are either already encoded (same
+    dtype as the pool, with k_scale_new / v_scale_new [n][Hkv]) or f16 /
+    bf16 rows that the library quantises on the device (scales written to
+    k_scale / v_scale)."""
     import torch
 
     device = k_pool.device
@@ -174,4 +179,5 @@ def write_kv(k_new, v_new, slots, k_pool, v_pool, *, k_scale_new=None, v_scale_n
     a.n = k_new.shape[0]
     a.num_kv_heads, a.head_dim, a.page_size, a.num_pages = Hkv, D, PS, num_pages
     a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
+    a.src_dtype = DTYPE_CODES[_dtype_name(k_new)]
     check(lib().pkv_write_kv(ctypes.byref(a), _stream_handle(stream, device)), "write_kv")

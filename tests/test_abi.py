@@ -146,12 +146,26 @@ def test_write_kv_rejects_bad_arguments():
     L = _lib.lib()
     w = WriteArgs()
     w.n, w.num_kv_heads, w.head_dim, w.page_size, w.num_pages = 4, 8, 96, 64, 16
-    w.kv_dtype = _lib.PKV_BF16
+    w.kv_dtype = w.src_dtype = _lib.PKV_BF16
     assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_UNSUPPORTED
     w.head_dim = 128
     assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_INVALID_ARG  # null pointers
     w.n = 0
     assert L.pkv_write_kv(ctypes.byref(w), None) == 0                         # nothing to do
+    # rows of another type: only f16 / bf16 into an int8 / fp8 pool (quantised)
+    w.src_dtype = _lib.PKV_F16
+    assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_UNSUPPORTED  # bf16 pool
+    w.kv_dtype, w.src_dtype = _lib.PKV_I8, _lib.PKV_FP8_E4M3
+    assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_UNSUPPORTED  # fp8 rows, int8 pool
+    w.n = 4
+    w.k_new = w.v_new = w.slots = w.k_pool = w.v_pool = FAKE
+    for kv in (_lib.PKV_I8, _lib.PKV_FP8_E4M3):
+        w.kv_dtype, w.src_dtype = kv, _lib.PKV_BF16
+        assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_INVALID_ARG  # no pool scales
+        w.src_dtype = kv
+        w.k_scale = w.v_scale = FAKE
+        assert L.pkv_write_kv(ctypes.byref(w), None) == _lib.PKV_ERR_INVALID_ARG  # encoded rows, no row scales
+        w.k_scale = w.v_scale = None
 
 
 @pytest.mark.skipif(_lib.lib().pkv_device_count() > 0, reason="a GPU is present")

@@ -126,3 +126,55 @@ def test_append_write_then_decode(Hq, Hkv, D, qd, kvd, PS, lens):
     compare(written, out, "decode over written pool")
     ref_layout = gpu_decode(case)
     assert torch.equal(out.view(torch.int16), ref_layout.view(torch.int16))
+
+
+@pytest.mark.parametrize("Hkv,D,src,kvd,PS", [
+    (8, 128, "bf16", "i8", 64),
+    (4, 64, "f16", "i8", 16),
+    (8, 128, "bf16", "fp8", 64),
+    (2, 64, "f16", "fp8", 16),
+    (16, 128, "f16", "fp8", 16),
+])
+def test_quantise_on_append_matches_oracle(Hkv, D, src, kvd, PS):
+    """f16 / bf16 rows written into an int8 / fp8 pool are quantised on the
+    device: codes and scales equal, bit for bit, the oracle's quantiser of
+    the same (exactly decoded) values, at the right slots."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth.make import _to_bits
+
+    note(f"quantise-on-append: Hkv {Hkv} D {D} {src}->{kvd} PS {PS}")
+    rng = np.random.default_rng(77)
+    n, num_pages = 150, 64
+    xs = []
+    for _ in range(2):   # K and V
+        x = rng.standard_normal((n, Hkv, D)).astype(np.float32) * 2.0
+        x[0] = 0.0                          # all-zero rows: the scale floor
+        x[1, :, 5] = 300.0                  # outliers
+        x[2] *= 1e-6                        # below the floor
+        bits = _to_bits(x, src)
+        exact = (bits.view(np.float16).astype(np.float32) if src == "f16"
+                 else (bits.astype(np.uint32) << 16).view(np.float32))
+        xs.append((bits, exact))
+    slots = rng.permutation(num_pages * PS)[:n].astype(np.int64)
+    dev = "cuda"
+    shape = (num_pages, Hkv, PS, D)
+    kv_t = torch_dtype(kvd)
+    pools = [torch.zeros(shape, dtype=torch.uint8, device=dev).view(kv_t) for _ in range(2)]
+    scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+    new = [_as_torch(b, src, dev) for b, _ in xs]
+    pkv.write_kv(new[0], new[1], torch.from_numpy(slots).to(dev), pools[0], pools[1],
+                 k_scale=scales[0], v_scale=scales[1])
+    torch.cuda.synchronize()
+    for (bits, exact), pool, sc in zip(xs, pools, scales):
+        codes, s = oracle.quantize_rows(exact, kvd)
+        want_pool = np.zeros(shape, dtype=np.uint8)
+        want_sc = np.zeros(shape[:3], dtype=np.float32)
+        oracle.scatter_rows(want_pool, slots, codes.view(np.uint8))
+        oracle.scatter_rows(want_sc[..., None], slots, s[..., None])
+        got_pool = pool.view(torch.uint8).cpu().numpy()
+        got_sc = sc.cpu().numpy()
+        bad = np.argwhere(got_pool != want_pool)
+        assert bad.size == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
+        assert np.array_equal(got_sc.view(np.uint32), want_sc.view(np.uint32))
