@@ -157,3 +157,92 @@ def test_gqa_saving_figure():
 def test_long_context_config_is_about_2p1_gb_per_layer():
     # batch 4 x 131072 tokens, 8 KV heads, head_dim 128, bf16, one layer
     assert kv_bytes(1, 8, 128, 131072, 4, 16) == 2_147_483_648
+
+
+# --------------------------------------------------------------------------
+# Block reuse: shared pages, owner counts, copy-on-write of a partly filled
+# shared last page.
+
+def test_fork_and_copy_on_write_trace():
+    from oracle.pool_model import SharedLastPage
+
+    m = PagePoolModel(16, 6)                      # free list [0..5], pop from the end
+    assert m.allocate(0, 20)[:2] == [5 * 16, 5 * 16 + 1]
+    assert m.page_table[0] == [5, 4]
+    m.fork(0, 1)
+    assert m.page_table[1] == [5, 4] and m.refcount == {5: 2, 4: 2}
+    # the last page holds 4 of 16 tokens and is shared: the plain append refuses
+    with pytest.raises(SharedLastPage):
+        m.append_tokens(1, 1)
+    slots, copy = m.append_tokens_cow(1, 1)
+    assert copy == (4, 3)                          # page 4 copied to the next free page, 3
+    assert m.page_table[1] == [5, 3] and slots == [3 * 16 + 4]
+    assert m.refcount == {5: 2, 4: 1, 3: 1}
+    # the parent is now the last page's only owner: it writes in place
+    assert m.append_tokens_cow(0, 1) == ([4 * 16 + 4], None)
+    # 12 more tokens fill page 3 exactly; the next append needs a new page, no copy
+    m.append_tokens_cow(1, 11)
+    assert m.token_count[1] == 32
+    m.fork(1, 2)
+    assert m.append_tokens_cow(2, 1) == ([2 * 16], None)   # full shared last page: no copy
+    assert m.page_table[2] == [5, 3, 2]
+    assert m.free_pages == [0, 1]
+    m.release(0)
+    assert m.free_pages == [0, 1, 4]               # page 5 still owned by 1 and 2
+    m.release(1)
+    assert m.free_pages == [0, 1, 4]               # pages 5 and 3 still owned by 2
+    m.release(2)
+    assert m.free_pages == [0, 1, 4, 5, 3, 2]
+    assert m.refcount == {}
+
+
+def test_copy_on_write_is_all_or_nothing():
+    m = PagePoolModel(4, 3)
+    m.allocate(0, 6)                               # pages [2, 1], one free
+    m.fork(0, 1)
+    with pytest.raises(OutOfPages):
+        m.append_tokens_cow(1, 3)                  # copy (1 page) + overflow (1 page) > 1 free
+    assert m.page_table[1] == [2, 1] and m.free_pages == [0] and m.refcount == {2: 2, 1: 2}
+
+
+fork_ops = st.lists(st.tuples(st.sampled_from(["alloc", "append", "append_cow", "release", "fork"]),
+                              st.integers(0, 4), st.integers(0, 40), st.integers(0, 4)),
+                    max_size=50)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.sampled_from([1, 4, 16]), st.integers(1, 24), fork_ops)
+def test_owner_counts_hold_after_any_operation_sequence(ps, num_pages, seq):
+    from oracle.pool_model import SharedLastPage
+
+    m = PagePoolModel(ps, num_pages)
+    for op, sid, n, other in seq:
+        before = (list(m.free_pages), {k: list(v) for k, v in m.page_table.items()}, dict(m.refcount))
+        try:
+            if op == "alloc":
+                m.allocate(sid, n)
+            elif op == "append":
+                m.append_tokens(sid, n)
+            elif op == "append_cow":
+                last_shared = (sid in m.page_table and m.token_count[sid] % ps != 0 and n > 0
+                               and m.refcount[m.page_table[sid][-1]] > 1)
+                old_last = m.page_table[sid][-1] if sid in m.page_table and m.page_table[sid] else None
+                _, copy = m.append_tokens_cow(sid, n)
+                assert (copy is not None) == last_shared
+                if copy is not None:
+                    assert copy[0] == old_last and copy[1] == before[0][-1]   # next free page
+            elif op == "fork":
+                m.fork(other, sid)
+            else:
+                m.release(sid)
+        except (OutOfPages, SequenceExists, UnknownSequence, SharedLastPage):
+            assert (m.free_pages, m.page_table, m.refcount) == before
+        owners = {}
+        for pages in m.page_table.values():
+            assert len(set(pages)) == len(pages)
+            for p in pages:
+                owners[p] = owners.get(p, 0) + 1
+        assert owners == m.refcount
+        assert sorted(list(owners) + m.free_pages) == list(range(num_pages))
+        for s, pages in m.page_table.items():
+            assert len(pages) == math.ceil(Fraction(m.token_count[s], ps))
