@@ -64,7 +64,9 @@ typedef enum pkv_status {
     PKV_ERR_SEQ_EXISTS = -4,  /* sequence id already allocated              */
     PKV_ERR_UNSUPPORTED = -5, /* shape / dtype outside the compiled set     */
     PKV_ERR_WORKSPACE = -6,   /* workspace missing or too small             */
-    PKV_ERR_DEVICE = -7       /* HIP runtime error (no device, bad launch)  */
+    PKV_ERR_DEVICE = -7,      /* HIP runtime error (no device, bad launch)  */
+    PKV_ERR_SHARED_PAGE = -8  /* the append needs a copy-on-write of a shared
+                                 page: use pkv_append_tokens_cow             */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -122,11 +124,34 @@ pkv_status pkv_seq_alloc(pkv_pool *pool, int64_t seq_id, int32_t num_tokens,
  * ceil((count + n_new - capacity) / page_size) new pages when the current
  * pages overflow.  OOM (checked before any page is taken) or NO_SEQ leave the
  * pool unchanged.  slots_out (host, may be NULL) receives the n_new slot ids
- * of the new tokens. */
+ * of the new tokens.  SHARED_PAGE (pool unchanged) if the sequence's last
+ * page is partly filled and shared with another sequence: that append needs
+ * the copy pkv_append_tokens_cow reports. */
 pkv_status pkv_append_tokens(pkv_pool *pool, int64_t seq_id, int32_t n_new,
                              int64_t *slots_out);
 
-/* Retires a sequence and pushes its pages back onto the free list.  NO_SEQ
+/* Block reuse (the KV-cache reuse and prefix caching of shared prompts that
+ * "TensorRT-LLM 推理加速实战", section 8, enables): pages may be owned by
+ * several sequences.
+ *
+ * pkv_seq_fork: child_id (new) gets parent_id's pages and token count; every
+ * page gains an owner.  NO_SEQ / SEQ_EXISTS leave the pool unchanged.
+ *
+ * pkv_append_tokens_cow: pkv_append_tokens that also handles a shared,
+ * partly filled last page: a fresh page (taken from the free list before any
+ * overflow pages) replaces it in this sequence, *copy_src / *copy_dst
+ * (host, may be NULL) receive (old page, new page), and the caller must copy
+ * the page's contents (pkv_copy_pages, every layer) before writing the new
+ * tokens; -1, -1 when no copy is needed.  OOM counts the copy's page too.
+ *
+ * pkv_page_owners: sequences holding a page (0 = free), -1 for a bad page. */
+pkv_status pkv_seq_fork(pkv_pool *pool, int64_t parent_id, int64_t child_id);
+pkv_status pkv_append_tokens_cow(pkv_pool *pool, int64_t seq_id, int32_t n_new, int64_t *slots_out,
+                                 int32_t *copy_src, int32_t *copy_dst);
+int32_t pkv_page_owners(const pkv_pool *pool, int32_t page);
+
+/* Retires a sequence; each of its pages loses an owner and returns to the
+ * free list (in the sequence's page order) when it has none left.  NO_SEQ
  * for an unknown id. */
 pkv_status pkv_seq_release(pkv_pool *pool, int64_t seq_id);
 
@@ -304,6 +329,28 @@ typedef struct pkv_write_args {
  * int8 / fp8 pool fed f16 / bf16 rows, quantises them first (see src_dtype).
  * Asynchronous on `stream`.  Slots must be distinct. */
 pkv_status pkv_write_kv(const pkv_write_args *args, void *stream);
+
+/* Device: whole-page copies for copy-on-write (pkv_append_tokens_cow), one
+ * layer's pools per call: for each pair i, page pairs[2i] is copied to page
+ * pairs[2i+1] in k_pool and v_pool (all KV heads, all slots) and, for int8 /
+ * fp8, in k_scale and v_scale.  pairs is a device int32 array; a pair naming
+ * a page outside [0, num_pages) is skipped.  Destination pages must be
+ * distinct and not sources.  Asynchronous on `stream`. */
+typedef struct pkv_copy_args {
+    void *k_pool;
+    void *v_pool;
+    float *k_scale;             /* int8 / fp8 only, else NULL                        */
+    float *v_scale;
+    const int32_t *pairs;       /* device [n][2]: (source page, destination page)    */
+    int32_t n;
+    int32_t num_pages;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t head_dim;
+    pkv_dtype kv_dtype;
+} pkv_copy_args;
+
+pkv_status pkv_copy_pages(const pkv_copy_args *args, void *stream);
 
 #ifdef __cplusplus
 }

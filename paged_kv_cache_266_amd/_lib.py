@@ -21,6 +21,7 @@ PKV_ERR_SEQ_EXISTS = -4
 PKV_ERR_UNSUPPORTED = -5
 PKV_ERR_WORKSPACE = -6
 PKV_ERR_DEVICE = -7
+PKV_ERR_SHARED_PAGE = -8
 
 PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "i8": PKV_I8, "fp8": PKV_FP8_E4M3}
@@ -33,7 +34,7 @@ EXPORTED = [
     "pkv_decode_workspace_bytes", "pkv_decode_counter_bytes", "pkv_decode_num_splits",
     "pkv_decode_validate",
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
-    "pkv_write_kv",
+    "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
 ]
 
 
@@ -72,6 +73,15 @@ class WriteArgs(ctypes.Structure):
     ]
 
 
+class CopyArgs(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("pairs", ctypes.c_void_p),
+        ("n", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+    ]
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
@@ -103,9 +113,15 @@ class DeviceError(PagedKVError):
     pass
 
 
+class SharedPage(PagedKVError):
+    """The append would write into a page other sequences share; use
+    append_tokens_cow and copy the page on the device."""
+
+
 _EXC = {PKV_ERR_OOM: KVCacheOOM, PKV_ERR_NO_SEQ: UnknownSequence,
         PKV_ERR_SEQ_EXISTS: SequenceExists, PKV_ERR_UNSUPPORTED: Unsupported,
-        PKV_ERR_WORKSPACE: WorkspaceError, PKV_ERR_DEVICE: DeviceError}
+        PKV_ERR_WORKSPACE: WorkspaceError, PKV_ERR_DEVICE: DeviceError,
+        PKV_ERR_SHARED_PAGE: SharedPage}
 
 _lib = None
 
@@ -154,6 +170,14 @@ def _declare(L):
         getattr(L, name).argtypes = [P(DecodeArgs), vp]
     L.pkv_write_kv.restype = ci
     L.pkv_write_kv.argtypes = [P(WriteArgs), vp]
+    L.pkv_seq_fork.restype = ci
+    L.pkv_seq_fork.argtypes = [vp, i64, i64]
+    L.pkv_append_tokens_cow.restype = ci
+    L.pkv_append_tokens_cow.argtypes = [vp, i64, i32, P(i64), P(i32), P(i32)]
+    L.pkv_page_owners.restype = i32
+    L.pkv_page_owners.argtypes = [vp, i32]
+    L.pkv_copy_pages.restype = ci
+    L.pkv_copy_pages.argtypes = [P(CopyArgs), vp]
     return L
 
 

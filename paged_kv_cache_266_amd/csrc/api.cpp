@@ -228,6 +228,7 @@ extern "C" const char *pkv_status_string(pkv_status s)
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_DEVICE: return "device error";
+    case PKV_ERR_SHARED_PAGE: return "append needs a copy of a shared page";
     }
     return "unknown status";
 }
@@ -362,4 +363,37 @@ extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)
     p.kv_dtype = a->kv_dtype;
     int err = launch_write_kv(p, stream);
     return err ? device_fail(err, "pkv_write_kv") : PKV_OK;
+}
+
+extern "C" pkv_status pkv_copy_pages(const pkv_copy_args *a, void *stream)
+{
+    clear_error();
+    if (!a)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: null argument struct");
+    if (a->n < 0 || a->num_pages <= 0 || a->num_kv_heads <= 0 || a->page_size <= 0 || a->head_dim <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: bad sizes");
+    if (a->kv_dtype != PKV_F16 && a->kv_dtype != PKV_BF16 && a->kv_dtype != PKV_I8 &&
+        a->kv_dtype != PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_pages: unknown kv dtype");
+    if (a->n == 0)
+        return PKV_OK;
+    const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
+    if (!a->k_pool || !a->v_pool || !a->pairs || (byte_kv && (!a->k_scale || !a->v_scale)))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: null device pointer");
+    const int64_t page_bytes =
+        (int64_t)a->num_kv_heads * a->page_size * a->head_dim * (byte_kv ? 1 : 2);
+    if (!aligned16(a->k_pool) || !aligned16(a->v_pool) || page_bytes % 16 || ((uintptr_t)a->pairs & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: pools must be 16-byte aligned");
+    CopyParams p{};
+    p.k_pool = a->k_pool;
+    p.v_pool = a->v_pool;
+    p.k_scale = byte_kv ? a->k_scale : nullptr;
+    p.v_scale = byte_kv ? a->v_scale : nullptr;
+    p.pairs = a->pairs;
+    p.n = a->n;
+    p.num_pages = a->num_pages;
+    p.page_bytes = page_bytes;
+    p.page_scales = (int64_t)a->num_kv_heads * a->page_size;
+    int err = launch_copy_pages(p, stream);
+    return err ? device_fail(err, "pkv_copy_pages") : PKV_OK;
 }

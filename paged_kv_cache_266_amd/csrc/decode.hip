@@ -1215,6 +1215,29 @@ __global__ __launch_bounds__(64) void write_kv_quant_kernel(WriteParams p)
     }
 }
 
+// ---- page copies (copy-on-write of shared pages) -------------------------------
+
+__global__ __launch_bounds__(256) void copy_pages_kernel(CopyParams p)
+{
+    const int64_t chunks = p.page_bytes / 16;
+    const int64_t total = (int64_t)p.n * chunks;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx / chunks, c = idx % chunks;
+        const int32_t src = p.pairs[2 * i], dst = p.pairs[2 * i + 1];
+        if (src < 0 || src >= p.num_pages || dst < 0 || dst >= p.num_pages)
+            continue;
+        const size_t so = (size_t)src * p.page_bytes + (size_t)c * 16;
+        const size_t d_o = (size_t)dst * p.page_bytes + (size_t)c * 16;
+        *reinterpret_cast<u32x4 *>((char *)p.k_pool + d_o) = *reinterpret_cast<const u32x4 *>((const char *)p.k_pool + so);
+        *reinterpret_cast<u32x4 *>((char *)p.v_pool + d_o) = *reinterpret_cast<const u32x4 *>((const char *)p.v_pool + so);
+        if (p.k_scale && c < p.page_scales) {
+            p.k_scale[(size_t)dst * p.page_scales + c] = p.k_scale[(size_t)src * p.page_scales + c];
+            p.v_scale[(size_t)dst * p.page_scales + c] = p.v_scale[(size_t)src * p.page_scales + c];
+        }
+    }
+}
+
 // ---- dispatch -------------------------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -1292,6 +1315,17 @@ static int launch_quant(const WriteParams &p, hipStream_t s)
     const void *fn = p.kv_dtype == I8 ? (const void *)&write_kv_quant_kernel<D, SRC, I8>
                                       : (const void *)&write_kv_quant_kernel<D, SRC, FP8>;
     return (int)hipLaunchKernel(fn, dim3(blocks), dim3(64), args, 0, s);
+}
+
+int launch_copy_pages(const CopyParams &p, void *stream)
+{
+    const int64_t total = (int64_t)p.n * (p.page_bytes / 16);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65535)
+        blocks = 65535;
+    void *args[] = {const_cast<CopyParams *>(&p)};
+    return (int)hipLaunchKernel((const void *)&copy_pages_kernel, dim3((unsigned)blocks), dim3(256), args, 0,
+                                (hipStream_t)stream);
 }
 
 int launch_write_kv(const WriteParams &p, void *stream)

@@ -82,4 +82,18 @@ int launch_decode_partitions(const DecodeParams &p, int head_dim, int page_size,
 int launch_splitk_reduce(const DecodeParams &p, int head_dim, int q_dtype, void *stream);
 int launch_write_kv(const WriteParams &p, void *stream);
 
+struct CopyParams {
+    void *k_pool;
+    void *v_pool;
+    float *k_scale;
+    float *v_scale;
+    const int32_t *pairs;
+    int32_t n;
+    int32_t num_pages;
+    int64_t page_bytes;    // bytes of one page of one pool (all heads)
+    int64_t page_scales;   // scales per page (all heads), 0 without scales
+};
+
+int launch_copy_pages(const CopyParams &p, void *stream);
+
 }  // namespace pkv

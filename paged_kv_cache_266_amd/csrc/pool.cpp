@@ -6,6 +6,12 @@
 // mutating call checks everything first and then commits, so an error leaves
 // the pool exactly as it was (the section's sketch would orphan popped pages
 // on a mid-allocation failure, and its append never checks for exhaustion).
+//
+// Block reuse: a page may be owned by several sequences (pkv_seq_fork); it
+// returns to the free list with its last owner.  Appending into a partly
+// filled shared last page first replaces it, in the appending sequence, by a
+// fresh page (taken before any overflow pages) whose contents the caller
+// copies on the device (pkv_copy_pages).
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -22,6 +28,7 @@ struct pkv_pool {
         int32_t tokens = 0;
     };
     std::unordered_map<int64_t, Seq> seqs;
+    std::vector<int32_t> owners;     // per page: sequences holding it (0 = free)
 };
 
 using pkv::fail;
@@ -41,6 +48,7 @@ extern "C" pkv_status pkv_pool_create(const pkv_pool_desc *desc, pkv_pool **out)
     p->num_pages = desc->num_pages;
     p->page_size = desc->page_size;
     p->free_list.resize((size_t)desc->num_pages);
+    p->owners.assign((size_t)desc->num_pages, 0);
     if (desc->initial_free_order) {
         std::vector<char> seen((size_t)desc->num_pages, 0);
         for (int32_t i = 0; i < desc->num_pages; ++i) {
@@ -89,6 +97,7 @@ extern "C" pkv_status pkv_seq_alloc(pkv_pool *pool, int64_t seq_id, int32_t num_
     s.pages.reserve((size_t)need);
     for (int64_t i = 0; i < need; ++i) {
         s.pages.push_back(pool->free_list.back());
+        pool->owners[(size_t)pool->free_list.back()] = 1;
         pool->free_list.pop_back();
     }
     s.tokens = num_tokens;
@@ -97,32 +106,89 @@ extern "C" pkv_status pkv_seq_alloc(pkv_pool *pool, int64_t seq_id, int32_t num_
     return PKV_OK;
 }
 
+// Append n_new tokens; *copy_src / *copy_dst receive the page pair to copy
+// (-1, -1 when none).  With allow_copy false an append that needs a copy is
+// refused (PKV_ERR_SHARED_PAGE).
+static pkv_status append(pkv_pool *pool, int64_t seq_id, int32_t n_new, int64_t *slots_out, bool allow_copy,
+                         int32_t *copy_src, int32_t *copy_dst, const char *who)
+{
+    if (!pool || n_new < 0)
+        return fail(PKV_ERR_INVALID_ARG, "append: null pool or negative token count");
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end())
+        return fail(PKV_ERR_NO_SEQ, "append: unknown sequence id");
+    pkv_pool::Seq &s = it->second;
+    const int64_t usage = s.tokens;
+    const int64_t capacity = (int64_t)s.pages.size() * pool->page_size;
+    if (usage + n_new > INT32_MAX)
+        return fail(PKV_ERR_INVALID_ARG, "append: token count overflows int32");
+    const bool copy = n_new > 0 && usage % pool->page_size != 0 && pool->owners[(size_t)s.pages.back()] > 1;
+    if (copy && !allow_copy)
+        return fail(PKV_ERR_SHARED_PAGE, who);
+    const int64_t over = usage + n_new > capacity ? ceil_div(usage + n_new - capacity, pool->page_size) : 0;
+    if (over + (copy ? 1 : 0) > (int64_t)pool->free_list.size())
+        return fail(PKV_ERR_OOM, "append: not enough free pages");
+    int32_t src = -1, dst = -1;
+    if (copy) {
+        src = s.pages.back();
+        dst = pool->free_list.back();
+        pool->free_list.pop_back();
+        pool->owners[(size_t)src] -= 1;
+        pool->owners[(size_t)dst] = 1;
+        s.pages.back() = dst;
+    }
+    for (int64_t i = 0; i < over; ++i) {
+        s.pages.push_back(pool->free_list.back());
+        pool->owners[(size_t)pool->free_list.back()] = 1;
+        pool->free_list.pop_back();
+    }
+    s.tokens = (int32_t)(usage + n_new);
+    write_slots(s, pool->page_size, (int32_t)usage, n_new, slots_out);
+    if (copy_src)
+        *copy_src = src;
+    if (copy_dst)
+        *copy_dst = dst;
+    return PKV_OK;
+}
+
 extern "C" pkv_status pkv_append_tokens(pkv_pool *pool, int64_t seq_id, int32_t n_new,
                                         int64_t *slots_out)
 {
     pkv::clear_error();
-    if (!pool || n_new < 0)
-        return fail(PKV_ERR_INVALID_ARG, "pkv_append_tokens: null pool or negative token count");
-    auto it = pool->seqs.find(seq_id);
+    return append(pool, seq_id, n_new, slots_out, false, nullptr, nullptr,
+                  "pkv_append_tokens: the last page is shared and partly filled; "
+                  "use pkv_append_tokens_cow");
+}
+
+extern "C" pkv_status pkv_append_tokens_cow(pkv_pool *pool, int64_t seq_id, int32_t n_new,
+                                            int64_t *slots_out, int32_t *copy_src, int32_t *copy_dst)
+{
+    pkv::clear_error();
+    return append(pool, seq_id, n_new, slots_out, true, copy_src, copy_dst, "");
+}
+
+extern "C" pkv_status pkv_seq_fork(pkv_pool *pool, int64_t parent_id, int64_t child_id)
+{
+    pkv::clear_error();
+    if (!pool)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_seq_fork: null pool");
+    auto it = pool->seqs.find(parent_id);
     if (it == pool->seqs.end())
-        return fail(PKV_ERR_NO_SEQ, "pkv_append_tokens: unknown sequence id");
-    pkv_pool::Seq &s = it->second;
-    int64_t usage = s.tokens;
-    int64_t capacity = (int64_t)s.pages.size() * pool->page_size;
-    if (usage + n_new > INT32_MAX)
-        return fail(PKV_ERR_INVALID_ARG, "pkv_append_tokens: token count overflows int32");
-    if (usage + n_new > capacity) {
-        int64_t need = ceil_div(usage + n_new - capacity, pool->page_size);
-        if (need > (int64_t)pool->free_list.size())
-            return fail(PKV_ERR_OOM, "pkv_append_tokens: not enough free pages");
-        for (int64_t i = 0; i < need; ++i) {
-            s.pages.push_back(pool->free_list.back());
-            pool->free_list.pop_back();
-        }
-    }
-    s.tokens = (int32_t)(usage + n_new);
-    write_slots(s, pool->page_size, (int32_t)usage, n_new, slots_out);
+        return fail(PKV_ERR_NO_SEQ, "pkv_seq_fork: unknown parent sequence id");
+    if (pool->seqs.count(child_id))
+        return fail(PKV_ERR_SEQ_EXISTS, "pkv_seq_fork: child sequence id already allocated");
+    pkv_pool::Seq child = it->second;   // copy before inserting (insertion may rehash)
+    for (int32_t pg : child.pages)
+        pool->owners[(size_t)pg] += 1;
+    pool->seqs.emplace(child_id, std::move(child));
     return PKV_OK;
+}
+
+extern "C" int32_t pkv_page_owners(const pkv_pool *pool, int32_t page)
+{
+    if (!pool || page < 0 || page >= pool->num_pages)
+        return -1;
+    return pool->owners[(size_t)page];
 }
 
 extern "C" pkv_status pkv_seq_release(pkv_pool *pool, int64_t seq_id)
@@ -134,7 +200,8 @@ extern "C" pkv_status pkv_seq_release(pkv_pool *pool, int64_t seq_id)
     if (it == pool->seqs.end())
         return fail(PKV_ERR_NO_SEQ, "pkv_seq_release: unknown sequence id");
     for (int32_t pg : it->second.pages)
-        pool->free_list.push_back(pg);
+        if (--pool->owners[(size_t)pg] == 0)
+            pool->free_list.push_back(pg);
     pool->seqs.erase(it);
     return PKV_OK;
 }

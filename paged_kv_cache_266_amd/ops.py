@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional
 
-from ._lib import DTYPE_CODES, DecodeArgs, WriteArgs, check, lib
+from ._lib import DTYPE_CODES, CopyArgs, DecodeArgs, WriteArgs, check, lib
 
 
 def _dtype_name(t) -> str:
@@ -181,3 +181,26 @@ def write_kv(k_new, v_new, slots, k_pool, v_pool, *, k_scale_new=None, v_scale_n
     a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
     a.src_dtype = DTYPE_CODES[_dtype_name(k_new)]
     check(lib().pkv_write_kv(ctypes.byref(a), _stream_handle(stream, device)), "write_kv")
+
+
+def copy_pages(pairs, k_pool, v_pool, *, k_scale=None, v_scale=None, stream=None) -> None:
+    """Copy whole pages (all KV heads) of one layer's pools: pairs is an
+    int32 device tensor [n][2] of (source page, destination page), as the
+    copy-on-write of append_tokens_cow reports them."""
+    import torch
+
+    device = k_pool.device
+    for t, n in ((pairs, "pairs"), (k_pool, "k_pool"), (v_pool, "v_pool"), (k_scale, "k_scale"),
+                 (v_scale, "v_scale")):
+        _check_tensor(t, n, device)
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    num_pages, Hkv, PS, D = k_pool.shape
+    a = CopyArgs()
+    a.k_pool, a.v_pool = _ptr(k_pool), _ptr(v_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.pairs = _ptr(pairs)
+    a.n = pairs.shape[0]
+    a.num_pages, a.num_kv_heads, a.page_size, a.head_dim = num_pages, Hkv, PS, D
+    a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
+    check(lib().pkv_copy_pages(ctypes.byref(a), _stream_handle(stream, device)), "copy_pages")

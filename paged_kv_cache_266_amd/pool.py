@@ -67,6 +67,24 @@ class KVPool:
               "append_tokens")
         return slots[:n_new]
 
+    def append_tokens_cow(self, seq_id: int, n_new: int):
+        """Grow a sequence whose last page may be shared.  Returns (slots,
+        copy) where copy is (old page, new page) to copy on the device before
+        writing the new tokens, or None."""
+        slots = np.empty(max(n_new, 1), dtype=np.int64)
+        src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        check(lib().pkv_append_tokens_cow(self._h, seq_id, n_new,
+                                          slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                          ctypes.byref(src), ctypes.byref(dst)), "append_tokens_cow")
+        return slots[:n_new], (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        """New sequence child_id sharing parent_id's pages (prefix reuse)."""
+        check(lib().pkv_seq_fork(self._h, parent_id, child_id), "fork")
+
+    def page_owners(self, page: int) -> int:
+        return int(lib().pkv_page_owners(self._h, page))
+
     def release(self, seq_id: int) -> None:
         check(lib().pkv_seq_release(self._h, seq_id), "release")
 

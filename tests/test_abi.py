@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 def test_abi_version_and_status_strings():
     L = _lib.lib()
     assert L.pkv_abi_version() == 1
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert L.pkv_status_string(code).decode()
     assert L.pkv_status_string(-99).decode() == "unknown status"
 

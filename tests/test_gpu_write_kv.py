@@ -178,3 +178,91 @@ def test_quantise_on_append_matches_oracle(Hkv, D, src, kvd, PS):
         bad = np.argwhere(got_pool != want_pool)
         assert bad.size == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
         assert np.array_equal(got_sc.view(np.uint32), want_sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "i8"])
+def test_prefix_sharing_with_copy_on_write(kvd):
+    """A prompt written once, shared by three forks; each fork appends its
+    own tokens into the partly filled shared last page (copy-on-write: the
+    pool hands out a fresh page, pkv_copy_pages copies it, the new tokens go
+    there), then the parent appends in place.  Every sequence decodes to the
+    oracle's answer on its own logical K/V, and the prefix pages stay shared."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth.make import _to_bits
+
+    Hq, Hkv, D, PS, num_pages = 8, 2, 128, 16, 40
+    note(f"prefix sharing: {kvd} KV, PS {PS}")
+    rng = np.random.default_rng(123)
+    dev = "cuda"
+    byte = kvd == "i8"
+    shape = (num_pages, Hkv, PS, D)
+    pools = [torch.zeros(shape, dtype=torch.uint8 if byte else torch.bfloat16, device=dev) for _ in range(2)]
+    if byte:
+        pools = [p.view(torch.int8) for p in pools]
+    scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)] if byte else [None, None]
+    host = [np.zeros(shape, dtype=np.int8 if byte else np.uint16) for _ in range(2)]
+    host_sc = [np.zeros(shape[:3], dtype=np.float32) for _ in range(2)]
+    def write(slots, n):
+        bits = [_to_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32), "bf16") for _ in range(2)]
+        k_src, v_src = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in bits)
+        pkv.write_kv(k_src, v_src, torch.from_numpy(np.asarray(slots, dtype=np.int64)).to(dev),
+                     pools[0], pools[1], k_scale=scales[0], v_scale=scales[1])
+        for which in range(2):
+            if byte:
+                exact = (bits[which].astype(np.uint32) << 16).view(np.float32)
+                codes, sc = oracle.quantize_rows(exact, "i8")
+                oracle.scatter_rows(host[which], np.asarray(slots), codes)
+                oracle.scatter_rows(host_sc[which][..., None], np.asarray(slots), sc[..., None])
+            else:
+                oracle.scatter_rows(host[which], np.asarray(slots), bits[which])
+
+    def copy(pair):
+        pkv.copy_pages(torch.tensor([pair], dtype=torch.int32, device=dev), pools[0], pools[1],
+                       k_scale=scales[0], v_scale=scales[1])
+        for which in range(2):
+            host[which][pair[1]] = host[which][pair[0]]
+            host_sc[which][pair[1]] = host_sc[which][pair[0]]
+
+    with pkv.KVPool(num_pages, PS) as pool:
+        write(pool.allocate(0, 100), 100)             # 7 pages, the last holds 4 tokens
+        prefix_pages = pool.pages(0)
+        for child in (1, 2, 3):
+            pool.fork(0, child)
+        copies = []
+        for child, n_new in ((1, 5), (2, 17), (3, 1)):
+            with pytest.raises(pkv.SharedPage):
+                pool.append_tokens(child, n_new)
+            slots, pair = pool.append_tokens_cow(child, n_new)
+            assert pair is not None and pair[0] == prefix_pages[-1]
+            copy(pair)
+            copies.append(pair)
+            write(slots, n_new)
+        slots, pair = pool.append_tokens_cow(0, 3)   # the parent is the page's last owner now
+        assert pair is None
+        write(slots, 3)
+        for child in (1, 2, 3):
+            assert pool.pages(child)[:6] == prefix_pages[:6]      # full prefix pages stay shared
+        assert all(pool.page_owners(p) == 4 for p in prefix_pages[:6])
+        ids = [0, 1, 2, 3]
+        bt, ctx = pool.block_tables(ids, 8)
+    torch.cuda.synchronize()
+    assert list(ctx) == [103, 105, 117, 101]
+
+    cfg = small_config(Hq, Hkv, D, "bf16", kvd, PS, tuple(int(c) for c in ctx), num_pages=num_pages)
+    case = make_case(cfg, seed=5)
+    written = dataclasses.replace(
+        case, block_tables=bt, used_pages=np.arange(num_pages, dtype=np.int32),
+        page_index=np.arange(num_pages, dtype=np.int32), k_pages=host[0], v_pages=host[1],
+        k_scale=host_sc[0] if byte else None, v_scale=host_sc[1] if byte else None)
+    # the device pools hold exactly the host mirror (writes and page copies)
+    for which in range(2):
+        got = pools[which].view(torch.int8 if byte else torch.int16).cpu().numpy()
+        assert np.array_equal(got.view(host[which].dtype), host[which])
+    q = upload(case, dev).q
+    out = pkv.paged_attn_decode(q, pools[0], pools[1], torch.from_numpy(bt).to(dev),
+                                torch.from_numpy(ctx).to(dev), case.scale,
+                                max_context_len=int(ctx.max()), k_scale=scales[0], v_scale=scales[1])
+    torch.cuda.synchronize()
+    compare(written, out, "forked sequences")

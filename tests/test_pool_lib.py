@@ -56,6 +56,51 @@ def test_library_pool_matches_model(ps, num_pages, rnd, seq):
             assert (bt_m == bt_l).all() and (lens_m == lens_l).all()
 
 
+fork_ops = st.lists(st.tuples(st.sampled_from(["alloc", "append", "append_cow", "release", "fork"]),
+                              st.integers(0, 5), st.integers(0, 70), st.integers(0, 5)), max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.sampled_from([16, 5]), st.integers(1, 20), st.randoms(use_true_random=False), fork_ops)
+def test_library_pool_with_sharing_matches_model(ps, num_pages, rnd, seq):
+    """Forks, owner counts and copy-on-write appends: the C pool returns the
+    model's slots and copy pairs and holds the model's state after every
+    operation, errors included."""
+    from oracle.pool_model import SharedLastPage
+
+    exc = dict(MODEL_EXC)
+    exc[SharedLastPage] = pkv.SharedPage
+    order = list(range(num_pages))
+    rnd.shuffle(order)
+    model = PagePoolModel(ps, num_pages, initial_free_order=order)
+    with pkv.KVPool(num_pages, ps, initial_free_order=order) as pool:
+        for op, sid, n, other in seq:
+            fn_m = {"alloc": lambda: model.allocate(sid, n),
+                    "append": lambda: model.append_tokens(sid, n),
+                    "append_cow": lambda: model.append_tokens_cow(sid, n),
+                    "release": lambda: model.release(sid),
+                    "fork": lambda: model.fork(other, sid)}[op]
+            fn_l = {"alloc": lambda: pool.allocate(sid, n),
+                    "append": lambda: pool.append_tokens(sid, n),
+                    "append_cow": lambda: pool.append_tokens_cow(sid, n),
+                    "release": lambda: pool.release(sid),
+                    "fork": lambda: pool.fork(other, sid)}[op]
+            try:
+                want = fn_m()
+            except (OutOfPages, SequenceExists, UnknownSequence, SharedLastPage) as e:
+                with pytest.raises(exc[type(e)]):
+                    fn_l()
+            else:
+                got = fn_l()
+                if op == "append_cow":
+                    assert list(got[0]) == want[0] and got[1] == want[1]
+                elif want is not None:
+                    assert list(got) == want
+            same_state(pool, model)
+            for page in range(num_pages):
+                assert pool.page_owners(page) == model.refcount.get(page, 0)
+
+
 def test_pool_rejects_bad_descriptors():
     with pytest.raises(pkv.PagedKVError):
         pkv.KVPool(0, 16)
