@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct layer buffers cycled through (0 = enough for >= 1 GB of KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="decode: the decode step (default); append: write every token of the workload "
+                         "into the pools with pkv_write_kv (quantising f16/bf16 rows for int8/fp8 pools)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -139,11 +142,18 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(case, min_seconds: float):
+def cpu_baseline(case, min_seconds: float, got, tol: float):
+    """The cpu_baseline leg: the fp64 oracle on the whole workload, timed on
+    this host's cores.  Its first (untimed) pass also gives the reference
+    output that the GPU's first launch is checked against (the parity of the
+    benchmarked launch configuration)."""
+    import numpy as np
     import oracle
 
     threads = oracle.default_threads()
-    oracle.paged_decode(case, n_threads=threads)          # warm-up
+    ref = oracle.paged_decode(case, n_threads=threads)    # warm-up, and the parity reference
+    max_err = float(np.abs(got - ref).max())
+    parity = {"max_abs_err": max_err, "tol": tol, "ok": bool(max_err <= tol)}
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.paged_decode(case, n_threads=threads)
@@ -160,7 +170,7 @@ def cpu_baseline(case, min_seconds: float):
                     break
     except OSError:
         pass
-    return {
+    return parity, {
         "value": round(case.bytes_alg() * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
@@ -169,6 +179,144 @@ def cpu_baseline(case, min_seconds: float):
                   f"{reps} fp64 layer-steps in {el:.1f} s, {el / reps * 1e6:.0f} us per layer-step; "
                   f"{cpu_model}",
     }
+
+
+def cpu_baseline_append(rows_f32, kind: str, got_codes, got_scales, min_seconds: float):
+    """The cpu_baseline leg of the append benchmark: the oracle's quantiser
+    over every appended row (its first pass is also the parity reference:
+    codes and scales must match bit for bit), timed on this host."""
+    import numpy as np
+    import oracle
+
+    codes, sc = oracle.quantize_rows(rows_f32, kind)
+    parity = {"rows": int(sc.size), "bit_exact": bool(
+        np.array_equal(np.asarray(got_codes).view(np.uint8), codes.view(np.uint8))
+        and np.array_equal(np.asarray(got_scales).view(np.uint32), sc.view(np.uint32)))}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantize_rows(rows_f32, kind)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    moved = rows_f32.size * (2 + 1) + sc.size * 4
+    return parity, {"value": round(moved * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle", "sample": f"{sc.size} rows of one pool (K), {reps} passes in {el:.1f} s"}
+
+
+def bench_append(args) -> None:
+    """Throughput of pkv_write_kv over a whole workload's tokens (a prefill's
+    worth of K/V, every KV head): rows in the query type, quantised on the
+    device when the pool is int8 / fp8, else copied.  Also times
+    pkv_copy_pages (the copy-on-write page copy) over a batch of pages."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth import CONFIGS
+    from synth.device import torch_dtype
+    from synth.make import _to_bits, draw_context_lens
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.config]
+    rng = np.random.default_rng(cfg.seed)
+    lens = draw_context_lens(cfg, rng)
+    n = int(lens.sum())
+    Hkv, D, PS = cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    src_t, kv_t = cfg.q_dtype, cfg.kv_dtype
+    byte = kv_t in ("i8", "fp8")
+    if not byte and kv_t != src_t:
+        raise SystemExit("a 16-bit pool takes rows of its own type")
+    e = 1 if byte else 2
+    dev = "cuda"
+    with pkv.KVPool(cfg.num_pages, PS, initial_free_order=rng.permutation(cfg.num_pages)) as pool:
+        slots = np.concatenate([pool.allocate(b, int(m)) for b, m in enumerate(lens)])
+    bits = [_to_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32), src_t) for _ in range(2)]
+    new = [torch.from_numpy(b.view(np.int16)).view(torch_dtype(src_t)).to(dev) for b in bits]
+    shape = (cfg.num_pages, Hkv, PS, D)
+    if byte:
+        pools = [torch.zeros(shape, dtype=torch.uint8, device=dev).view(torch_dtype(kv_t)) for _ in range(2)]
+        scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+    else:
+        pools = [torch.zeros(shape, dtype=torch_dtype(kv_t), device=dev) for _ in range(2)]
+        scales = [None, None]
+    slots_d = torch.from_numpy(slots).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pkv.write_kv(new[0], new[1], slots_d, pools[0], pools[1], k_scale=scales[0], v_scale=scales[1])
+
+    step()
+    torch.cuda.synchronize()
+    pg, off = slots // PS, slots % PS
+    got = [p.view(torch.uint8 if byte else torch.int16).cpu().numpy()[pg, :, off, :] for p in pools]
+    parity, baseline = None, None
+    if byte:
+        if not args.no_cpu_baseline:
+            rows = ((bits[0].astype(np.uint32) << 16).view(np.float32) if src_t == "bf16"
+                    else bits[0].view(np.float16).astype(np.float32))
+            parity, baseline = cpu_baseline_append(rows, kv_t, got[0], scales[0].cpu().numpy()[pg, :, off],
+                                                   args.cpu_seconds)
+    else:
+        parity = {"rows": n * Hkv * 2, "bit_exact": bool(all(
+            np.array_equal(g.view(np.uint16), b) for g, b in zip(got, bits)))}
+    del got
+
+    def timed(fn, steps):
+        fn()
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < WARMUP_SECONDS:
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps, ev[0].elapsed_time(ev[1]) / steps
+
+    ms, ev_ms = timed(step, args.steps)
+    moved = 2 * n * Hkv * D * (2 + e) + (2 * n * Hkv * 4 if byte else 0)
+
+    # page copies: the used pages' first half copied onto free pages
+    used = np.unique(pg)
+    free = np.setdiff1d(np.arange(cfg.num_pages), used)
+    ncopy = int(min(len(used), len(free), 4096))
+    pairs = torch.from_numpy(np.stack([used[:ncopy], free[:ncopy]], 1).astype(np.int32)).to(dev)
+
+    def copy_step():
+        pkv.copy_pages(pairs, pools[0], pools[1], k_scale=scales[0], v_scale=scales[1])
+
+    copy_step()
+    torch.cuda.synchronize()
+    src_i, dst_i = pairs[:, 0].long(), pairs[:, 1].long()
+    copy_ok = all(bool(torch.equal(t[dst_i], t[src_i]))
+                  for t in [p.view(torch.uint8) for p in pools] + [x for x in scales if x is not None])
+    cms, cev_ms = timed(copy_step, args.steps)
+    page_bytes = Hkv * PS * D * e + (Hkv * PS * 4 if byte else 0)
+    cmoved = 2 * 2 * ncopy * page_bytes
+
+    rec = {
+        "metric": "K/V append (pkv_write_kv) HBM GB/s (% of 8 TB/s peak)",
+        "value": round(moved / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "dtype": f"{src_t}->{kv_t}", "data": "synthetic",
+        "config": {"workload": f"append_{cfg.name}", "tokens": n, "num_kv_heads": Hkv, "head_dim": D,
+                   "page_size": PS, "bytes_alg_per_step": moved, "quantise": byte},
+        "pct_of_peak": round(100 * moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "event_us": round(ev_ms * 1e3, 2),
+        "parity": parity,
+        "copy_pages": {"pages": ncopy, "bytes_alg": cmoved, "us": round(cms * 1e3, 2),
+                       "event_us": round(cev_ms * 1e3, 2),
+                       "GB/s": round(cmoved / (cms * 1e-3) / 1e9, 2), "bit_exact": copy_ok},
+    }
+    if baseline is not None:
+        rec["cpu_baseline"] = baseline
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -196,6 +344,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(COPY_CALIBRATION_MIB)
+        return
+    if args.op == "append":
+        bench_append(args)
         return
 
     import paged_kv_cache_266_amd as pkv
@@ -251,17 +402,16 @@ def main():
         check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
         ev[1].record(stream)
 
-    # parity of the benchmarked launch configuration against the oracle,
-    # checked first: the oracle keeps the GPU idle for seconds, so it must
-    # not sit between the warm-up and the timed region
-    import oracle
-
+    # the cpu_baseline leg (which also checks the first launch's output) runs
+    # first: the oracle keeps the GPU idle for seconds, so it must not sit
+    # between the warm-up and the timed region
     step(0)
     torch.cuda.synchronize()
     got = out.to(torch.float64).cpu().numpy()
-    ref = oracle.paged_decode(case)
-    max_err = float(np.abs(got - ref).max())
     tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}[cfg.kv_dtype]
+    parity, baseline = {"ok": None, "note": "not checked: --no-cpu-baseline"}, None
+    if not args.no_cpu_baseline:
+        parity, baseline = cpu_baseline(case, args.cpu_seconds, got, tol)
 
     # W warm-up steps, then more (untimed) until the GPU has been busy for
     # WARMUP_SECONDS, so that clocks have settled before the timed region
@@ -333,11 +483,11 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
         },
-        "parity": {"max_abs_err": max_err, "tol": tol, "ok": bool(max_err <= tol)},
+        "parity": parity,
         "source_digest": source_digest(),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if baseline is not None:
+        result["cpu_baseline"] = baseline
     print(json.dumps(result), flush=True)
 
 
