@@ -309,7 +309,7 @@ typedef struct pkv_write_args {
     void *v_pool;
     float *k_scale;             /* device pool scales; int8 / fp8 only, else NULL    */
     float *v_scale;
-    int32_t n;                  /* tokens to write, >= 0                             */
+    int32_t n;                  /* tokens to write, >= 0; n * num_kv_heads < 2^31    */
     int32_t num_kv_heads;
     int32_t head_dim;           /* 64 or 128                                        */
     int32_t page_size;
@@ -335,7 +335,8 @@ pkv_status pkv_write_kv(const pkv_write_args *args, void *stream);
  * pairs[2i+1] in k_pool and v_pool (all KV heads, all slots) and, for int8 /
  * fp8, in k_scale and v_scale.  pairs is a device int32 array; a pair naming
  * a page outside [0, num_pages) is skipped.  Destination pages must be
- * distinct and not sources.  Asynchronous on `stream`. */
+ * distinct and not sources.  INVALID_ARG when n times the page's 16 KiB
+ * tiles (per pool) reaches 2^32.  Asynchronous on `stream`. */
 typedef struct pkv_copy_args {
     void *k_pool;
     void *v_pool;

@@ -333,6 +333,8 @@ extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)
     if (a->src_dtype != a->kv_dtype && !quantise)
         return fail(PKV_ERR_UNSUPPORTED, "pkv_write_kv: src_dtype must equal kv_dtype, or be f16 / bf16 "
                                          "with an int8 / fp8 pool");
+    if ((int64_t)a->n * a->num_kv_heads >= ((int64_t)1 << 31))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_write_kv: n * num_kv_heads must be below 2^31");
     if (a->n == 0)
         return PKV_OK;
     if (!a->k_new || !a->v_new || !a->slots || !a->k_pool || !a->v_pool)
@@ -384,6 +386,9 @@ extern "C" pkv_status pkv_copy_pages(const pkv_copy_args *a, void *stream)
         (int64_t)a->num_kv_heads * a->page_size * a->head_dim * (byte_kv ? 1 : 2);
     if (!aligned16(a->k_pool) || !aligned16(a->v_pool) || page_bytes % 16 || ((uintptr_t)a->pairs & 3u))
         return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: pools must be 16-byte aligned");
+    const int64_t tiles = (page_bytes / 16 + kCopyTileChunks - 1) / kCopyTileChunks;
+    if ((int64_t)a->n * tiles > (int64_t)0xFFFFFFFF)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: too many pairs for the page size in one call");
     CopyParams p{};
     p.k_pool = a->k_pool;
     p.v_pool = a->v_pool;

@@ -1123,117 +1123,208 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DecodeParams p)
 }
 
 // ---- K/V scatter for appended tokens -----------------------------------------
+//
+// A token row (one token, one KV head) is handled by the lanes of one group,
+// each lane owning 16 bytes of it, so that a wave reads whole consecutive rows
+// of the caller's [n][Hkv][D] arrays.  Row indices are 32-bit (the host
+// rejects n * Hkv >= 2^31); a slot's page and offset use a 32-bit division
+// whenever the slot fits in 32 bits.
 
+// Pool row of `slot` (page-major: [page][Hkv][page_size]) for KV head g;
+// false for a slot outside the pool, which is skipped.
+__device__ __forceinline__ bool pool_row(int64_t slot, u32 g, int32_t page_size, int32_t num_pages,
+                                         int32_t num_kv_heads, size_t &row)
+{
+    if (slot < 0 || slot >= (int64_t)num_pages * page_size)
+        return false;
+    u32 page, off;
+    if (slot <= (int64_t)0xFFFFFFFF) {
+        page = (u32)slot / (u32)page_size;
+        off = (u32)slot - page * (u32)page_size;
+    } else {
+        const int64_t pg = slot / page_size;
+        page = (u32)pg;
+        off = (u32)(slot - pg * page_size);
+    }
+    row = ((size_t)page * (u32)num_kv_heads + g) * (u32)page_size + off;
+    return true;
+}
+
+// Copy form: rows already in the pool's type (with their scales for int8 /
+// fp8).  CPR = 16-byte chunks per row.
+template <int CPR>
 __global__ __launch_bounds__(256) void write_kv_kernel(WriteParams p)
 {
-    const int chunks = p.row_bytes / 16;
-    const size_t total = (size_t)p.n * p.num_kv_heads * chunks;
-    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (size_t)gridDim.x * blockDim.x) {
-        const int c = (int)(idx % chunks);
-        const size_t ig = idx / chunks;
-        const int g = (int)(ig % p.num_kv_heads);
-        const size_t i = ig / p.num_kv_heads;
-        const int64_t slot = p.slots[i];
-        if (slot < 0 || slot >= (int64_t)p.num_pages * p.page_size)
+    constexpr u32 RPB = 256 / CPR;   // rows per block and pass
+    const u32 c = threadIdx.x % CPR;
+    const u32 rows = (u32)p.n * (u32)p.num_kv_heads;
+    const u32x4 *kn = reinterpret_cast<const u32x4 *>(p.k_new);
+    const u32x4 *vn = reinterpret_cast<const u32x4 *>(p.v_new);
+    u32x4 *kp = reinterpret_cast<u32x4 *>(p.k_pool);
+    u32x4 *vp = reinterpret_cast<u32x4 *>(p.v_pool);
+    for (u32 row = blockIdx.x * RPB + threadIdx.x / CPR; row < rows; row += gridDim.x * RPB) {
+        const u32x4 kx = kn[(size_t)row * CPR + c];
+        const u32x4 vx = vn[(size_t)row * CPR + c];
+        const u32 i = row / (u32)p.num_kv_heads, g = row - i * (u32)p.num_kv_heads;
+        size_t dst;
+        if (!pool_row(p.slots[i], g, p.page_size, p.num_pages, p.num_kv_heads, dst))
             continue;
-        const int64_t page = slot / p.page_size, off = slot % p.page_size;
-        const size_t row = ((size_t)page * p.num_kv_heads + g) * p.page_size + off;
-        const size_t src = (i * p.num_kv_heads + g) * (size_t)p.row_bytes + (size_t)c * 16;
-        const size_t dst = row * p.row_bytes + (size_t)c * 16;
-        *reinterpret_cast<u32x4 *>((char *)p.k_pool + dst) =
-            *reinterpret_cast<const u32x4 *>((const char *)p.k_new + src);
-        *reinterpret_cast<u32x4 *>((char *)p.v_pool + dst) =
-            *reinterpret_cast<const u32x4 *>((const char *)p.v_new + src);
+        kp[dst * CPR + c] = kx;
+        vp[dst * CPR + c] = vx;
         if (c == 0 && p.k_scale) {
-            p.k_scale[row] = p.k_scale_new[i * p.num_kv_heads + g];
-            p.v_scale[row] = p.v_scale_new[i * p.num_kv_heads + g];
+            p.k_scale[dst] = p.k_scale_new[row];
+            p.v_scale[dst] = p.v_scale_new[row];
         }
     }
 }
 
 // ---- quantise-on-append ------------------------------------------------------
 //
-// One wave per appended row (one token of one KV head) of f16 / bf16 values
-// into an int8 or fp8 pool: the row's exact max magnitude (wave reduction),
-// s = max(amax, 1e-5) / Q in fp32 (Q = 127 for int8, 448 for E4M3), then
-// each value's code: round-half-to-even of x / s (int8 clipped to +-127;
-// fp8 through the hardware converter, which rounds to nearest even; |x / s|
-// never exceeds 448 by more than the rounding of s, which still rounds to
-// 448).  The scale goes to the pool's scale array at the row's slot.
+// f16 / bf16 rows into an int8 or fp8 pool.  Each row of D values is held by
+// D / 8 lanes, 8 values each; the row's exact max magnitude is reduced over
+// those lanes, s = max(amax, 1e-5) / Q in fp32 (Q = 127 for int8, 448 for
+// E4M3, correctly rounded division), then each value's code is
+// round-half-to-even of x / s (int8 clipped to +-127; fp8 through the
+// hardware converter, which rounds to nearest even; |x / s| never exceeds 448
+// by more than the rounding of s, which still rounds to 448).  The scale goes
+// to the pool's scale array at the row's slot.
+
+constexpr int kRowHalfMirror = 0x141;   // row_half_mirror: j -> 7 - j within 8 lanes
+
+// max over aligned groups of L lanes (L = 8 or 16); every lane gets its group's
+template <int L>
+__device__ __forceinline__ float group_max(float x)
+{
+    x = fmaxf(x, dpp<kQuadXor1>(x));
+    x = fmaxf(x, dpp<kQuadXor2>(x));
+    x = fmaxf(x, dpp<kRowHalfMirror>(x));
+    if constexpr (L == 16)
+        x = fmaxf(x, dpp<kRowRor8>(x));
+    return x;
+}
+
+template <int L, int SRC, int KVT>
+__device__ __forceinline__ void quantise8(u32x4 w, u32 &lo, u32 &hi, float &s)
+{
+    constexpr float kQ = KVT == I8 ? 127.0f : 448.0f;
+    float x[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const u32 bits = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+        x[e] = SRC == BF16 ? __builtin_bit_cast(float, bits << 16)
+                           : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+        amax = fmaxf(amax, fabsf(x[e]));
+    }
+    amax = group_max<L>(amax);
+    s = fmaxf(amax, 1e-5f) / kQ;
+    u32 word[2];
+    if constexpr (KVT == I8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32 v = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float r = fminf(fmaxf(rintf(x[4 * h + e] / s), -127.0f), 127.0f);
+                v |= ((u32)(int)r & 0xFFu) << (8 * e);
+            }
+            word[h] = v;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h] / s, x[4 * h + 1] / s, 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2] / s, x[4 * h + 3] / s, v, true);
+            word[h] = (u32)v;
+        }
+    }
+    lo = word[0];
+    hi = word[1];
+}
 
 template <int D, int SRC, int KVT>
-__global__ __launch_bounds__(64) void write_kv_quant_kernel(WriteParams p)
+__global__ __launch_bounds__(256) void write_kv_quant_kernel(WriteParams p)
 {
-    constexpr int EPL = D / 64;   // values per lane
-    constexpr float kQ = KVT == I8 ? 127.0f : 448.0f;
-    const int lane = threadIdx.x;
-    const size_t rows = (size_t)p.n * p.num_kv_heads;
-    for (size_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const size_t i = row / p.num_kv_heads;
-        const int g = (int)(row % p.num_kv_heads);
-        const int64_t slot = p.slots[i];
-        if (slot < 0 || slot >= (int64_t)p.num_pages * p.page_size)
-            continue;
-        const int64_t page = slot / p.page_size, off = slot % p.page_size;
-        const size_t dst_row = ((size_t)page * p.num_kv_heads + g) * p.page_size + off;
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const uint16_t *src = reinterpret_cast<const uint16_t *>(which ? p.v_new : p.k_new) + row * D + EPL * lane;
-            float x[EPL];
-            float amax = 0.0f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const u32 bits = src[e];
-                x[e] = SRC == BF16 ? __builtin_bit_cast(float, bits << 16)
-                                   : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-                amax = fmaxf(amax, fabsf(x[e]));
-            }
-            amax = wave_max(amax);
-            const float s = fmaxf(amax, 1e-5f) / kQ;
-            uint8_t code[EPL];
-            if constexpr (KVT == I8) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const float r = fminf(fmaxf(rintf(x[e] / s), -127.0f), 127.0f);
-                    code[e] = (uint8_t)(int8_t)r;
-                }
-            } else {
-                const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, EPL > 1 ? x[EPL - 1] / s : 0.0f, 0, false);
-                code[0] = (uint8_t)(packed & 0xff);
-                if constexpr (EPL > 1)
-                    code[EPL - 1] = (uint8_t)((packed >> 8) & 0xff);
-            }
-            uint8_t *dst = reinterpret_cast<uint8_t *>(which ? p.v_pool : p.k_pool) + dst_row * D + EPL * lane;
-            if constexpr (EPL == 2)
-                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(code[0] | (code[1] << 8));
-            else
-                dst[0] = code[0];
-            if (lane == 0)
-                (which ? p.v_scale : p.k_scale)[dst_row] = s;
-        }
+    constexpr u32 L = D / 8;         // lanes per row
+    constexpr u32 RPB = 256 / L;     // rows per block and pass
+    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+    const u32 sub = threadIdx.x % L;
+    const u32 rows = (u32)p.n * (u32)p.num_kv_heads;
+    const u32x4 *kn = reinterpret_cast<const u32x4 *>(p.k_new);
+    const u32x4 *vn = reinterpret_cast<const u32x4 *>(p.v_new);
+    u32x2 *kp = reinterpret_cast<u32x2 *>(p.k_pool);
+    u32x2 *vp = reinterpret_cast<u32x2 *>(p.v_pool);
+    for (u32 row = blockIdx.x * RPB + threadIdx.x / L; row < rows; row += gridDim.x * RPB) {
+        const u32x4 kx = kn[(size_t)row * L + sub];
+        const u32x4 vx = vn[(size_t)row * L + sub];
+        const u32 i = row / (u32)p.num_kv_heads, g = row - i * (u32)p.num_kv_heads;
+        size_t dst;
+        if (!pool_row(p.slots[i], g, p.page_size, p.num_pages, p.num_kv_heads, dst))
+            continue;   // the whole group skips: its lanes share the row
+        u32 lo, hi;
+        float s;
+        quantise8<L, SRC, KVT>(kx, lo, hi, s);
+        kp[dst * L + sub] = u32x2{lo, hi};
+        if (sub == 0)
+            p.k_scale[dst] = s;
+        quantise8<L, SRC, KVT>(vx, lo, hi, s);
+        vp[dst * L + sub] = u32x2{lo, hi};
+        if (sub == 0)
+            p.v_scale[dst] = s;
     }
 }
 
 // ---- page copies (copy-on-write of shared pages) -------------------------------
+//
+// Block b copies tile b % tiles_per_page of pair b / tiles_per_page: kCopyUnroll
+// 16-byte chunks per thread of K and of V (all loads issued before the
+// stores), plus the same index range of the page's scales.
+
+constexpr int kCopyUnroll = kCopyTileChunks / 256;
+constexpr int kCopyTile = kCopyTileChunks;
+static_assert(kCopyUnroll * 256 == kCopyTile, "a tile is kCopyUnroll chunks per thread");
 
 __global__ __launch_bounds__(256) void copy_pages_kernel(CopyParams p)
 {
-    const int64_t chunks = p.page_bytes / 16;
-    const int64_t total = (int64_t)p.n * chunks;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = idx / chunks, c = idx % chunks;
-        const int32_t src = p.pairs[2 * i], dst = p.pairs[2 * i + 1];
+    const u32 tiles = (u32)p.tiles_per_page;
+    const u32 total = (u32)p.n * tiles;
+    for (u32 b = blockIdx.x; b < total; b += gridDim.x) {
+        const u32 pair = b / tiles, tile = b - pair * tiles;
+        const int32_t src = p.pairs[2 * pair], dst = p.pairs[2 * pair + 1];
         if (src < 0 || src >= p.num_pages || dst < 0 || dst >= p.num_pages)
             continue;
-        const size_t so = (size_t)src * p.page_bytes + (size_t)c * 16;
-        const size_t d_o = (size_t)dst * p.page_bytes + (size_t)c * 16;
-        *reinterpret_cast<u32x4 *>((char *)p.k_pool + d_o) = *reinterpret_cast<const u32x4 *>((const char *)p.k_pool + so);
-        *reinterpret_cast<u32x4 *>((char *)p.v_pool + d_o) = *reinterpret_cast<const u32x4 *>((const char *)p.v_pool + so);
-        if (p.k_scale && c < p.page_scales) {
-            p.k_scale[(size_t)dst * p.page_scales + c] = p.k_scale[(size_t)src * p.page_scales + c];
-            p.v_scale[(size_t)dst * p.page_scales + c] = p.v_scale[(size_t)src * p.page_scales + c];
+        const int64_t chunks = p.page_bytes / 16;
+        const int64_t c0 = (int64_t)tile * kCopyTile + threadIdx.x;
+        const u32x4 *ks = reinterpret_cast<const u32x4 *>((const char *)p.k_pool + (size_t)src * p.page_bytes);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>((const char *)p.v_pool + (size_t)src * p.page_bytes);
+        u32x4 *kd = reinterpret_cast<u32x4 *>((char *)p.k_pool + (size_t)dst * p.page_bytes);
+        u32x4 *vd = reinterpret_cast<u32x4 *>((char *)p.v_pool + (size_t)dst * p.page_bytes);
+        u32x4 kv[kCopyUnroll], vv[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t c = c0 + 256 * u;
+            if (c < chunks) {
+                kv[u] = ks[c];
+                vv[u] = vs[c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t c = c0 + 256 * u;
+            if (c < chunks) {
+                kd[c] = kv[u];
+                vd[c] = vv[u];
+            }
+        }
+        if (p.k_scale) {
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int64_t j = c0 + 256 * u;
+                if (j < p.page_scales) {
+                    p.k_scale[(size_t)dst * p.page_scales + j] = p.k_scale[(size_t)src * p.page_scales + j];
+                    p.v_scale[(size_t)dst * p.page_scales + j] = p.v_scale[(size_t)src * p.page_scales + j];
+                }
+            }
         }
     }
 }
@@ -1306,43 +1397,55 @@ int launch_splitk_reduce(const DecodeParams &p, int D, int qt, void *stream)
                                 (hipStream_t)stream);
 }
 
+static unsigned grid_for(size_t work, size_t per_block)
+{
+    const size_t blocks = (work + per_block - 1) / per_block;
+    return (unsigned)(blocks < 65535 ? blocks : 65535);
+}
+
 template <int D, int SRC>
 static int launch_quant(const WriteParams &p, hipStream_t s)
 {
     const size_t rows = (size_t)p.n * p.num_kv_heads;
-    const unsigned blocks = (unsigned)(rows < 65535 ? rows : 65535);
     void *args[] = {const_cast<WriteParams *>(&p)};
     const void *fn = p.kv_dtype == I8 ? (const void *)&write_kv_quant_kernel<D, SRC, I8>
                                       : (const void *)&write_kv_quant_kernel<D, SRC, FP8>;
-    return (int)hipLaunchKernel(fn, dim3(blocks), dim3(64), args, 0, s);
+    return (int)hipLaunchKernel(fn, dim3(grid_for(rows, 256 / (D / 8))), dim3(256), args, 0, s);
 }
 
 int launch_copy_pages(const CopyParams &p, void *stream)
 {
-    const int64_t total = (int64_t)p.n * (p.page_bytes / 16);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65535)
-        blocks = 65535;
-    void *args[] = {const_cast<CopyParams *>(&p)};
-    return (int)hipLaunchKernel((const void *)&copy_pages_kernel, dim3((unsigned)blocks), dim3(256), args, 0,
+    // chunks per page cover its scales too (a row has at least 16 bytes)
+    const int64_t chunks = p.page_bytes / 16;
+    CopyParams q = p;
+    q.tiles_per_page = (int32_t)((chunks + kCopyTile - 1) / kCopyTile);
+    if (q.tiles_per_page < 1 || p.page_scales > (int64_t)q.tiles_per_page * kCopyTile ||
+        (int64_t)p.n * q.tiles_per_page > (int64_t)0xFFFFFFFF)
+        return (int)hipErrorInvalidValue;
+    void *args[] = {&q};
+    return (int)hipLaunchKernel((const void *)&copy_pages_kernel,
+                                dim3(grid_for((size_t)p.n * q.tiles_per_page, 1)), dim3(256), args, 0,
                                 (hipStream_t)stream);
 }
 
 int launch_write_kv(const WriteParams &p, void *stream)
 {
+    hipStream_t s = (hipStream_t)stream;
     if (p.src_dtype != p.kv_dtype) {   // f16 / bf16 rows into an int8 / fp8 pool
-        hipStream_t s = (hipStream_t)stream;
         if (p.head_dim == 64)
             return p.src_dtype == BF16 ? launch_quant<64, BF16>(p, s) : launch_quant<64, F16>(p, s);
         return p.src_dtype == BF16 ? launch_quant<128, BF16>(p, s) : launch_quant<128, F16>(p, s);
     }
-    const size_t total = (size_t)p.n * p.num_kv_heads * (p.row_bytes / 16);
-    size_t blocks = (total + 255) / 256;
-    if (blocks > 65535)
-        blocks = 65535;
+    const size_t rows = (size_t)p.n * p.num_kv_heads;
     void *args[] = {const_cast<WriteParams *>(&p)};
-    return (int)hipLaunchKernel((const void *)&write_kv_kernel, dim3((unsigned)blocks), dim3(256), args, 0,
-                                (hipStream_t)stream);
+    const void *fn;
+    switch (p.row_bytes) {
+    case 64: fn = (const void *)&write_kv_kernel<4>; break;
+    case 128: fn = (const void *)&write_kv_kernel<8>; break;
+    case 256: fn = (const void *)&write_kv_kernel<16>; break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipLaunchKernel(fn, dim3(grid_for(rows, 256 / (p.row_bytes / 16))), dim3(256), args, 0, s);
 }
 
 }  // namespace pkv

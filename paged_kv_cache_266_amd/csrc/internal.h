@@ -92,7 +92,11 @@ struct CopyParams {
     int32_t num_pages;
     int64_t page_bytes;    // bytes of one page of one pool (all heads)
     int64_t page_scales;   // scales per page (all heads), 0 without scales
+    int32_t tiles_per_page;   // set by the launcher
 };
+
+// 16-byte chunks of one page that one block of copy_pages_kernel copies
+constexpr int kCopyTileChunks = 1024;
 
 int launch_copy_pages(const CopyParams &p, void *stream);
 

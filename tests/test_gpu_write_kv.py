@@ -266,3 +266,112 @@ def test_prefix_sharing_with_copy_on_write(kvd):
                                 max_context_len=int(ctx.max()), k_scale=scales[0], v_scale=scales[1])
     torch.cuda.synchronize()
     compare(written, out, "forked sequences")
+
+
+@pytest.mark.parametrize("Hkv,D,src,kvd,PS", [
+    (8, 128, "bf16", "bf16", 64),    # copy form, 16 chunks per row
+    (4, 64, "f16", "f16", 16),       # copy form, 8 chunks per row
+    (3, 64, "f16", "i8", 16),        # quantise, 8 lanes per row; odd head count
+    (8, 128, "bf16", "fp8", 64),     # quantise, 16 lanes per row
+])
+def test_append_many_rows_skips_out_of_range_slots(Hkv, D, src, kvd, PS):
+    """Thousands of rows (several grid passes and a ragged last block) with
+    slots -1 and num_pages * page_size among them: those rows are skipped,
+    every other row lands at its slot (bit for bit against the oracle's
+    quantiser and scatter), and nothing else in the pools changes."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth.make import _to_bits
+
+    note(f"append many rows: Hkv {Hkv} D {D} {src}->{kvd} PS {PS}")
+    rng = np.random.default_rng(4242)
+    n, num_pages = 3001, 256
+    slots = rng.permutation(num_pages * PS)[:n].astype(np.int64)
+    slots[7] = -1
+    slots[1000] = num_pages * PS
+    valid = (slots >= 0) & (slots < num_pages * PS)
+    dev = "cuda"
+    shape = (num_pages, Hkv, PS, D)
+    byte = kvd in ("i8", "fp8")
+    kv_t = torch_dtype(kvd)
+    fill = 0x5A
+    pools = [torch.full(shape, fill, dtype=torch.uint8, device=dev) for _ in range(2)]
+    if not byte:
+        pools = [torch.full((*shape[:3], 2 * D), fill, dtype=torch.uint8, device=dev) for _ in range(2)]
+    pools = [p.view(kv_t) for p in pools]
+    scales = [torch.full(shape[:3], -7.0, dtype=torch.float32, device=dev) for _ in range(2)] if byte else [None, None]
+    want = []
+    new = []
+    for _ in range(2):
+        x = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+        bits = _to_bits(x, src)
+        new.append(_as_torch(bits, src, dev))
+        row_bytes = D * (1 if byte else 2)
+        want_pool = np.full((*shape[:3], row_bytes), fill, dtype=np.uint8)
+        want_sc = np.full(shape[:3], -7.0, dtype=np.float32)
+        if byte:
+            exact = (bits.view(np.float16).astype(np.float32) if src == "f16"
+                     else (bits.astype(np.uint32) << 16).view(np.float32))
+            codes, s = oracle.quantize_rows(exact[valid], kvd)
+            oracle.scatter_rows(want_pool, slots[valid], codes.view(np.uint8))
+            oracle.scatter_rows(want_sc[..., None], slots[valid], s[..., None])
+        else:
+            oracle.scatter_rows(want_pool, slots[valid], bits[valid].view(np.uint8).reshape(-1, Hkv, row_bytes))
+        want.append((want_pool, want_sc))
+    pkv.write_kv(new[0], new[1], torch.from_numpy(slots).to(dev), pools[0], pools[1],
+                 k_scale=scales[0], v_scale=scales[1])
+    torch.cuda.synchronize()
+    for w, (want_pool, want_sc) in enumerate(want):
+        got = pools[w].view(torch.uint8).cpu().numpy().reshape(want_pool.shape)
+        bad = np.argwhere(got != want_pool)
+        assert bad.size == 0, f"pool {w}: {len(bad)} bytes differ, first at {tuple(bad[0])}"
+        if byte:
+            assert np.array_equal(scales[w].cpu().numpy().view(np.uint32), want_sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("Hkv,D,kvd,PS", [
+    (2, 64, "f16", 16),      # 4 KiB pages: one partial tile
+    (8, 128, "bf16", 64),    # 128 KiB pages: eight tiles
+    (3, 128, "i8", 16),      # 6 KiB pages with scales
+    (8, 128, "fp8", 64),     # 64 KiB pages with scales
+])
+def test_copy_pages_whole_pages(Hkv, D, kvd, PS):
+    """pkv_copy_pages copies whole pages (codes and scales, K and V) onto
+    their destinations; a pair naming a page outside the pool is skipped and
+    every other page is untouched."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    note(f"copy pages: Hkv {Hkv} D {D} {kvd} PS {PS}")
+    rng = np.random.default_rng(99)
+    num_pages = 300
+    byte = kvd in ("i8", "fp8")
+    e = 1 if byte else 2
+    dev = "cuda"
+    host = [rng.integers(0, 256, size=(num_pages, Hkv, PS, D * e), dtype=np.uint8) for _ in range(2)]
+    if byte and kvd == "fp8":
+        for h in host:
+            h[(h & 0x7F) == 0x7F] = 0x10      # no NaN codes
+    host_sc = [rng.standard_normal((num_pages, Hkv, PS)).astype(np.float32) for _ in range(2)]
+    pools = [torch.from_numpy(h).to(dev).view(torch_dtype(kvd)).view(num_pages, Hkv, PS, D) for h in host]
+    scales = [torch.from_numpy(h).to(dev) for h in host_sc] if byte else [None, None]
+    perm = rng.permutation(num_pages)
+    src, dst = perm[:100], perm[100:200]
+    pairs = np.stack([src, dst], 1).astype(np.int32)
+    pairs[5] = (-1, pairs[5, 1])             # skipped
+    pairs[6] = (pairs[6, 0], num_pages)      # skipped
+    pkv.copy_pages(torch.from_numpy(pairs).to(dev), pools[0], pools[1], k_scale=scales[0], v_scale=scales[1])
+    torch.cuda.synchronize()
+    for w in range(2):
+        want = host[w].copy()
+        want_sc = host_sc[w].copy()
+        for s_, d_ in pairs:
+            if 0 <= s_ < num_pages and 0 <= d_ < num_pages:
+                want[d_] = host[w][s_]
+                want_sc[d_] = host_sc[w][s_]
+        got = pools[w].view(torch.uint8).cpu().numpy().reshape(want.shape)
+        assert np.array_equal(got, want)
+        if byte:
+            assert np.array_equal(scales[w].cpu().numpy().view(np.uint32), want_sc.view(np.uint32))
