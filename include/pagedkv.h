@@ -236,7 +236,7 @@ typedef struct pkv_decode_args {
                                    (all sequences, all KV heads) are divided into this
                                    many equal contiguous shares, one per wave of a
                                    persistent grid.  0 = library default (4 waves per
-                                   compute unit, 8 for int8 KV);
+                                   compute unit, 8 for int8 / fp8 KV);
                                    always capped at the number of tiles the batch
                                    can have.                                         */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16; out has the same type       */

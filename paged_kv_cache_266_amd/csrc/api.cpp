@@ -66,7 +66,8 @@ static int32_t resolve_splits(const pkv_decode_args *a)
 {
     const int64_t tiles_per_seq = ((int64_t)a->max_context_len + kTileTokens - 1) / kTileTokens;
     const int64_t upper = std::max<int64_t>(1, (int64_t)a->batch * a->num_kv_heads * tiles_per_seq);
-    const int64_t per_cu = a->kv_dtype == PKV_I8 ? kDefaultWavesPerCUInt8 : kDefaultWavesPerCU;
+    const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
+    const int64_t per_cu = byte_kv ? kDefaultWavesPerCUByte : kDefaultWavesPerCU;
     const int64_t want = a->num_splits > 0 ? a->num_splits : per_cu * device_cu_count();
     return (int32_t)std::min<int64_t>(std::min<int64_t>(want, upper), 1 << 24);
 }

@@ -52,6 +52,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 #include <utility>
 
 #include "internal.h"
@@ -61,6 +62,7 @@ namespace {
 
 typedef uint32_t u32;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4;
+typedef __attribute__((ext_vector_type(2))) u32 u32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
@@ -222,6 +224,18 @@ __device__ __forceinline__ float2 fp8_pair(u32 w)
     return make_float2(v[0], v[1]);
 }
 
+// Two E4M3 codes of w (bytes 2*HI and 2*HI + 1) widened to a packed pair of
+// q's 16-bit type (v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1): exact, as
+// every E4M3 value is a bf16 and an f16 value.
+template <int QT, bool HI>
+__device__ __forceinline__ u32 fp8_pair16(u32 w)
+{
+    if constexpr (QT == BF16)
+        return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
 // Unsigned byte e of w as float (v_cvt_f32_ubyteN).
 template <int E>
 __device__ __forceinline__ float ubyte(u32 w) { return (float)((w >> (8 * E)) & 0xFFu); }
@@ -268,7 +282,6 @@ __device__ __forceinline__ void store_coherent4(float *base, int bytes, int voff
 
 __device__ __forceinline__ void store_coherent2(float *base, int bytes, int voff, float2 v)
 {
-    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), tile_rsrc((const char *)base, bytes),
                                           voff, 0, kCoherent);
 }
@@ -281,7 +294,6 @@ __device__ __forceinline__ float4 load_coherent4(const float *base, int bytes, i
 
 __device__ __forceinline__ float2 load_coherent2(const float *base, int bytes, int voff)
 {
-    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(tile_rsrc((const char *)base, bytes),
                                                                            voff, 0, kCoherent));
 }
@@ -305,10 +317,13 @@ struct Shape {
     static constexpr int PAGE = PS;                // tokens per page
     static constexpr int EB = KVT == I8 || KVT == FP8 ? 1 : 2;   // bytes per KV element
     static constexpr int ROW = D * EB;             // bytes per token row
-    static constexpr int R = ROW / 16;             // lanes per token row
+    // a lane's chunk of a row: 8 elements (16 bytes of 16-bit KV, 8 of byte KV)
+    static constexpr int CB = 8 * EB;              // bytes per lane chunk
+    using Chunk = std::conditional_t<CB == 16, u32x4, u32x2>;
+    static constexpr int R = ROW / CB;             // lanes per token row
     static constexpr int LEVELS = R == 16 ? 4 : R == 8 ? 3 : 2;
     static constexpr int TPI = 64 / R;             // tokens per load instruction
-    static constexpr int EPL = 16 / EB;            // elements per lane chunk
+    static constexpr int EPL = CB / EB;            // elements per lane chunk
     static constexpr int TILE_BYTES = PS * ROW;    // one (page, KV head) tile
     static constexpr int PPT = kTileTokens / PS;   // pages per 64-token tile
     static constexpr int PSTRIDE = 64 * G + (64 / R) * 4;  // floats in the p buffer
@@ -317,7 +332,7 @@ struct Shape {
     static_assert(kTileTokens % PS == 0, "tiles hold whole pages");
 };
 
-// Where the 16 bytes of chunk i of a 64-token tile come from, for this lane.
+// Where the bytes of chunk i of a 64-token tile come from, for this lane.
 // base[] is the (page, KV head) tile of each page of the tile (page 0 stands
 // in for a page that does not exist; nothing is read from it).  The lane's
 // byte offset within a page is the same for every chunk; the chunk's own
@@ -341,12 +356,17 @@ struct TileAddr {
     }
 
     template <int I>
-    __device__ __forceinline__ u32x4 load(int lane_off) const
+    __device__ __forceinline__ typename S::Chunk load(int lane_off) const
     {
         constexpr int pg = (I * S::TPI) / S::PAGE;
         constexpr int chunk_off = ((I * S::TPI) % S::PAGE) * S::ROW;
         const int voff = I < nvalid ? lane_off : kOutOfRange;
-        return __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(base[pg], S::TILE_BYTES), voff, chunk_off, kStreamingLoad);
+        if constexpr (S::CB == 16)
+            return __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(base[pg], S::TILE_BYTES), voff, chunk_off,
+                                                         kStreamingLoad);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b64(tile_rsrc(base[pg], S::TILE_BYTES), voff, chunk_off,
+                                                        kStreamingLoad);
     }
 };
 
@@ -571,7 +591,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // byte KV (int8 or fp8): one fp32 scale per token, q kept as fp32
     constexpr bool kByte = KVT == I8 || KVT == FP8;
     constexpr bool kI8 = KVT == I8;
-    constexpr int QW = kByte ? 8 : 4;   // dwords of q per head per lane
+    constexpr int QW = EPL / 2;         // dwords of q per head per lane
+    using Chunk = typename S::Chunk;
+    constexpr int CW = S::CB / 4;       // dwords per chunk
 
     __shared__ float s_p[S::PSTRIDE];
 
@@ -697,24 +719,24 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         }
     };
 
-    // q in the form the dot products use: packed pairs (16-bit KV) or fp32
-    // values (byte KV), for int8 with the -128 * sum(q) bias of the
-    // unsigned-byte trick.
-    u32 qw[G][4];
-    float qf[kByte ? G : 1][kByte ? 16 : 1];
+    // q in the form the dot products use: packed pairs (16-bit and fp8 KV,
+    // fp8 codes being widened to q's type) or fp32 values (int8 KV, with the
+    // -128 * sum(q) bias of the unsigned-byte trick).
+    u32 qw[G][QW];
+    float qf[kI8 ? G : 1][kI8 ? EPL : 1];
     float qbias[G];
     auto set_q = [&](const u32 (&raw)[G][QW]) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if constexpr (!kByte) {
+            if constexpr (!kI8) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < QW; ++v)
                     qw[h][v] = raw[h][v];
                 qbias[h] = 0.0f;
             } else {
                 float s = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < QW; ++e) {
                     qf[h][2 * e] = q_lo<QT>(raw[h][e]);
                     qf[h][2 * e + 1] = q_hi<QT>(raw[h][e]);
                     s += qf[h][2 * e] + qf[h][2 * e + 1];
@@ -741,13 +763,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // tile t, V of tile t, K of tile t+1, ...: each chunk's V load is issued
     // as soon as its K has been used, and the next tile's K as soon as its V
     // has been used -- across segment boundaries too.
-    const int lane_off = r * S::ROW + 16 * j;
+    const int lane_off = r * S::ROW + S::CB * j;
     int ph_cur[PPT], ph_nxt[PPT];
     pages_of(cur, ph_cur);
     TileAddr<S> ka, va;
     ka.set((const char *)p.k_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
     va.set((const char *)p.v_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
-    u32x4 ring[R];
+    Chunk ring[R];
     [&]<int... I>(std::integer_sequence<int, I...>) { ((ring[I] = ka.template load<I>(lane_off)), ...); }
         (std::make_integer_sequence<int, R>{});
     // int8 KV: the next segment's raw q is fetched a tile ahead (its fp32
@@ -795,38 +817,43 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (([&] {
                  float v[G];
-                 const u32x4 kc = ring[I];
+                 const Chunk kc = ring[I];
+                 u32 kw[CW];
+#pragma unroll
+                 for (int c = 0; c < CW; ++c)
+                     kw[c] = kc[c];
+                 u32 k16[KVT == FP8 ? QW : 1];
+                 if constexpr (KVT == FP8) {
+#pragma unroll
+                     for (int c = 0; c < CW; ++c) {
+                         k16[2 * c] = fp8_pair16<QT, false>(kw[c]);
+                         k16[2 * c + 1] = fp8_pair16<QT, true>(kw[c]);
+                     }
+                 }
 #pragma unroll
                  for (int h = 0; h < G; ++h) {
                      float a;
                      if constexpr (!kByte) {
-                         a = dot2<KVT>(kc.x, qw[h][0], 0.0f);
-                         a = dot2<KVT>(kc.y, qw[h][1], a);
-                         a = dot2<KVT>(kc.z, qw[h][2], a);
-                         a = dot2<KVT>(kc.w, qw[h][3], a);
-                     } else if constexpr (KVT == FP8) {
-                         // E4M3 pairs through the hardware converter
-                         const u32 wd[4] = {kc.x, kc.y, kc.z, kc.w};
                          a = 0.0f;
 #pragma unroll
-                         for (int q4 = 0; q4 < 4; ++q4) {
-                             const float2 lo = fp8_pair<false>(wd[q4]), hi = fp8_pair<true>(wd[q4]);
-                             a = fmaf(qf[h][4 * q4 + 0], lo.x, a);
-                             a = fmaf(qf[h][4 * q4 + 1], lo.y, a);
-                             a = fmaf(qf[h][4 * q4 + 2], hi.x, a);
-                             a = fmaf(qf[h][4 * q4 + 3], hi.y, a);
-                         }
+                         for (int c = 0; c < CW; ++c)
+                             a = dot2<KVT>(kw[c], qw[h][c], a);
+                     } else if constexpr (KVT == FP8) {
+                         // widened E4M3 pairs against q's packed pairs
+                         a = 0.0f;
+#pragma unroll
+                         for (int v2 = 0; v2 < QW; ++v2)
+                             a = dot2<QT>(k16[v2], qw[h][v2], a);
                      } else {
                          // code + 128 as unsigned bytes; the -128 * sum(q) bias restores the sign
-                         const u32 wd[4] = {kc.x ^ 0x80808080u, kc.y ^ 0x80808080u, kc.z ^ 0x80808080u,
-                                            kc.w ^ 0x80808080u};
                          a = qbias[h];
 #pragma unroll
-                         for (int q4 = 0; q4 < 4; ++q4) {
-                             a = fmaf(qf[h][4 * q4 + 0], ubyte<0>(wd[q4]), a);
-                             a = fmaf(qf[h][4 * q4 + 1], ubyte<1>(wd[q4]), a);
-                             a = fmaf(qf[h][4 * q4 + 2], ubyte<2>(wd[q4]), a);
-                             a = fmaf(qf[h][4 * q4 + 3], ubyte<3>(wd[q4]), a);
+                         for (int q4 = 0; q4 < CW; ++q4) {
+                             const u32 wd = kw[q4] ^ 0x80808080u;
+                             a = fmaf(qf[h][4 * q4 + 0], ubyte<0>(wd), a);
+                             a = fmaf(qf[h][4 * q4 + 1], ubyte<1>(wd), a);
+                             a = fmaf(qf[h][4 * q4 + 2], ubyte<2>(wd), a);
+                             a = fmaf(qf[h][4 * q4 + 3], ubyte<3>(wd), a);
                          }
                      }
                      v[h] = a;
@@ -878,13 +905,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                  for (int h = 0; h < G; ++h)
                      pv[h] = src[h];
-                 const u32x4 vc = ring[I];
+                 const Chunk vc = ring[I];
                  ring[I] = ka.template load<I>(lane_off);
                  float vf[EPL];
-                 const u32 wv[4] = {vc.x, vc.y, vc.z, vc.w};
+                 u32 wv[CW];
+#pragma unroll
+                 for (int c = 0; c < CW; ++c)
+                     wv[c] = vc[c];
                  if constexpr (KVT == FP8) {
 #pragma unroll
-                     for (int q4 = 0; q4 < 4; ++q4) {
+                     for (int q4 = 0; q4 < CW; ++q4) {
                          const float2 lo = fp8_pair<false>(wv[q4]), hi = fp8_pair<true>(wv[q4]);
                          vf[4 * q4 + 0] = lo.x;
                          vf[4 * q4 + 1] = lo.y;
@@ -893,7 +923,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                      }
                  } else if constexpr (kI8) {
 #pragma unroll
-                     for (int q4 = 0; q4 < 4; ++q4) {
+                     for (int q4 = 0; q4 < CW; ++q4) {
                          const u32 u = wv[q4] ^ 0x80808080u;
                          vf[4 * q4 + 0] = ubyte<0>(u);
                          vf[4 * q4 + 1] = ubyte<1>(u);
@@ -1247,7 +1277,6 @@ __global__ __launch_bounds__(256) void write_kv_quant_kernel(WriteParams p)
 {
     constexpr u32 L = D / 8;         // lanes per row
     constexpr u32 RPB = 256 / L;     // rows per block and pass
-    typedef __attribute__((ext_vector_type(2))) u32 u32x2;
     const u32 sub = threadIdx.x % L;
     const u32 rows = (u32)p.n * (u32)p.num_kv_heads;
     const u32x4 *kn = reinterpret_cast<const u32x4 *>(p.k_new);

@@ -18,12 +18,12 @@ pkv_status fail(pkv_status code, const char *msg);
 // Tokens per wave-iteration of the decode kernel.
 constexpr int kTileTokens = 64;
 // Default waves per compute unit of the persistent grid (measured on
-// MI355X): one per SIMD for 16-bit and fp8 KV, where a second co-resident
-// wave on a SIMD only slows the first (and the grid ends on the slower
-// one); two per SIMD for int8 KV, whose sign trick and conversions leave
-// more arithmetic to overlap with memory latency.
+// MI355X): one per SIMD for 16-bit KV, where a second co-resident wave on a
+// SIMD only slows the first (and the grid ends on the slower one); two per
+// SIMD for int8 and fp8 KV, whose conversions leave more arithmetic to
+// overlap with memory latency (fp8, Llama-3-8B shape: 67 vs 78 us).
 constexpr int kDefaultWavesPerCU = 4;
-constexpr int kDefaultWavesPerCUInt8 = 8;
+constexpr int kDefaultWavesPerCUByte = 8;
 
 enum DType : int { F16 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
 
