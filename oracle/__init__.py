@@ -10,6 +10,7 @@ Contents:
   (sequence, query head) units; loaded here through ctypes.
 * ``brute.py`` -- pure-Python contiguous attention (no pages) for tiny inputs.
 * ``pool_model.py`` -- the free-list page allocator, as a Python model.
+* ``sched_model.py`` -- the continuous-batching step driver over that pool.
 * ``kvsize.py`` -- the KV-cache size formula.
 """
 
