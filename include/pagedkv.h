@@ -353,6 +353,88 @@ typedef struct pkv_copy_args {
 
 pkv_status pkv_copy_pages(const pkv_copy_args *args, void *stream);
 
+/* ===================================================================== *
+ * Host: continuous-batching step driver over a pool.  One step follows
+ * "TensorRT-LLM 深度实战", section 3.2: finished sequences leave the batch
+ * and release their pages, waiting requests join while there is room (their
+ * prompt's pages are allocated), then every running sequence appends one
+ * token.  The clock, arrival steps, the static-batching alternative and the
+ * statistics follow the request simulator of the aiqz.cc TensorRT-LLM
+ * explainer ("连续批处理", "Python 演示").  Readings where those pages are
+ * silent:
+ *   - the waiting queue is served first come, first served, in submission
+ *     order; arrival steps must not decrease along it;
+ *   - a request reserves the pages of its whole life,
+ *     ceil((prompt_len + max_new_tokens) / page_size); the head of the queue
+ *     is admitted only when the free pages minus the pages still owed to
+ *     running sequences cover that, and nothing overtakes it -- so a running
+ *     sequence never runs out of pages (if the scheduler is the pool's only
+ *     user);
+ *   - PKV_SCHED_STATIC admits only into an empty batch;
+ *   - with nothing running and the head of the queue not yet arrived, the
+ *     clock jumps to its arrival; it advances by one per step that runs;
+ *   - the batch is listed in admission order.
+ * The pool must outlive the scheduler; the scheduler's sequences live in it
+ * (read their pages and block tables through the pool calls above).
+ * ===================================================================== */
+
+typedef struct pkv_sched pkv_sched;
+
+typedef enum pkv_sched_policy {
+    PKV_SCHED_CONTINUOUS = 0,
+    PKV_SCHED_STATIC = 1
+} pkv_sched_policy;
+
+/* max_batch >= 1 sequences run per step.  INVALID_ARG on bad arguments. */
+pkv_status pkv_sched_create(pkv_pool *pool, int32_t max_batch, pkv_sched_policy policy,
+                            pkv_sched **out);
+void pkv_sched_destroy(pkv_sched *sched);
+
+/* Queues a request: prompt_len >= 0 tokens already computed when it is
+ * admitted, then max_new_tokens >= 1 decode steps; it may be admitted from
+ * step arrive_step on.  INVALID_ARG for bad sizes or an arrival before the
+ * last queued one; SEQ_EXISTS if seq_id is queued, running or live in the
+ * pool; OOM if its reservation exceeds the whole pool.  Nothing changes on
+ * error. */
+pkv_status pkv_sched_submit(pkv_sched *sched, int64_t seq_id, int32_t prompt_len,
+                            int32_t max_new_tokens, int64_t arrive_step);
+
+/* Ends a request early (an end token): a running one retires at the next
+ * step, a queued one is dropped.  NO_SEQ if it is neither. */
+pkv_status pkv_sched_finish(pkv_sched *sched, int64_t seq_id);
+
+typedef struct pkv_sched_step_out {
+    int64_t step;               /* the clock of this step (after an idle jump)       */
+    int32_t n_running;          /* entries of seq_ids / new_slots / context_lens     */
+    int32_t n_admitted;         /* entries of admitted                               */
+    int32_t n_retired;          /* entries of retired                                */
+} pkv_sched_step_out;
+
+/* Runs one step.  Host output arrays of `capacity` >= max_batch entries:
+ * seq_ids (the batch), new_slots (the slot of each sequence's new token, to
+ * write its K/V at), context_lens (tokens after the append: what decode
+ * attends over), admitted (joined this step: their prompt K/V goes to the
+ * slots of tokens 0 .. prompt_len - 1), retired (left this step; their ids
+ * may be reused).  With nothing to run, n_running is 0 and the clock stays.
+ * INVALID_ARG for a short capacity or a NULL output (nothing changes); OOM
+ * if the pool, used outside the scheduler, cannot cover the step -- then
+ * only the retirements happened (n_retired and retired are valid). */
+pkv_status pkv_sched_step(pkv_sched *sched, int32_t capacity, int64_t *seq_ids,
+                          int64_t *new_slots, int32_t *context_lens, int64_t *admitted,
+                          int64_t *retired, pkv_sched_step_out *out);
+
+typedef struct pkv_sched_stats {
+    int64_t now;                /* the clock                                         */
+    int32_t waiting;            /* queued requests                                   */
+    int32_t running;            /* sequences in the batch (finished ones included
+                                   until the step that retires them)                 */
+    int64_t finished;           /* requests retired                                  */
+    int64_t wait_sum;           /* over retired requests: step of the last token
+                                   minus arrival step                                */
+} pkv_sched_stats;
+
+pkv_status pkv_sched_get_stats(const pkv_sched *sched, pkv_sched_stats *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,11 @@ EXPORTED = [
     "pkv_decode_validate",
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
     "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
+    "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
+    "pkv_sched_get_stats",
 ]
+
+PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC = 0, 1
 
 
 class PoolDesc(ctypes.Structure):
@@ -80,6 +84,16 @@ class CopyArgs(ctypes.Structure):
         ("n", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
     ]
+
+
+class SchedStepOut(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("n_running", ctypes.c_int32),
+                ("n_admitted", ctypes.c_int32), ("n_retired", ctypes.c_int32)]
+
+
+class SchedStats(ctypes.Structure):
+    _fields_ = [("now", ctypes.c_int64), ("waiting", ctypes.c_int32), ("running", ctypes.c_int32),
+                ("finished", ctypes.c_int64), ("wait_sum", ctypes.c_int64)]
 
 
 class PagedKVError(RuntimeError):
@@ -178,6 +192,18 @@ def _declare(L):
     L.pkv_page_owners.argtypes = [vp, i32]
     L.pkv_copy_pages.restype = ci
     L.pkv_copy_pages.argtypes = [P(CopyArgs), vp]
+    L.pkv_sched_create.restype = ci
+    L.pkv_sched_create.argtypes = [vp, i32, ci, P(vp)]
+    L.pkv_sched_destroy.restype = None
+    L.pkv_sched_destroy.argtypes = [vp]
+    L.pkv_sched_submit.restype = ci
+    L.pkv_sched_submit.argtypes = [vp, i64, i32, i32, i64]
+    L.pkv_sched_finish.restype = ci
+    L.pkv_sched_finish.argtypes = [vp, i64]
+    L.pkv_sched_step.restype = ci
+    L.pkv_sched_step.argtypes = [vp, i32, P(i64), P(i64), P(i32), P(i64), P(i64), P(SchedStepOut)]
+    L.pkv_sched_get_stats.restype = ci
+    L.pkv_sched_get_stats.argtypes = [vp, P(SchedStats)]
     return L
 
 

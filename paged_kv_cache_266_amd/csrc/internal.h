@@ -15,6 +15,10 @@ namespace pkv {
 void clear_error();
 pkv_status fail(pkv_status code, const char *msg);
 
+// Pool geometry, for the scheduler.
+int32_t pool_page_size(const pkv_pool *pool);
+int32_t pool_num_pages(const pkv_pool *pool);
+
 // Tokens per wave-iteration of the decode kernel.
 constexpr int kTileTokens = 64;
 // Default waves per compute unit of the persistent grid (measured on

@@ -71,6 +71,9 @@ extern "C" pkv_status pkv_pool_create(const pkv_pool_desc *desc, pkv_pool **out)
 
 extern "C" void pkv_pool_destroy(pkv_pool *pool) { delete pool; }
 
+int32_t pkv::pool_page_size(const pkv_pool *pool) { return pool->page_size; }
+int32_t pkv::pool_num_pages(const pkv_pool *pool) { return pool->num_pages; }
+
 static void write_slots(const pkv_pool::Seq &s, int32_t ps, int32_t first, int32_t count,
                         int64_t *slots_out)
 {
