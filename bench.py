@@ -45,9 +45,11 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct layer buffers cycled through (0 = enough for >= 1 GB of KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "serve"], default="decode",
                     help="decode: the decode step (default); append: write every token of the workload "
-                         "into the pools with pkv_write_kv (quantising f16/bf16 rows for int8/fp8 pools)")
+                         "into the pools with pkv_write_kv (quantising f16/bf16 rows for int8/fp8 pools); "
+                         "serve: the continuous-batching loop (scheduler step, K/V appends, decode of the "
+                         "mixed batch) over a backlog of requests of the workload's shape")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -319,6 +321,129 @@ def bench_append(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+def bench_serve(args) -> None:
+    """The serving loop over one layer's pools: each step runs the native
+    scheduler (retire, admit, one token per running sequence), writes the
+    admitted prompts' K/V and every new token's K/V at their slots, builds the
+    block tables, and decodes the mixed batch.  Requests: a backlog of
+    4 x batch requests whose prompt lengths follow the workload's length law
+    and which generate 32..256 tokens each (uniform), all arrived at step 0,
+    at most `batch` running.  K steps are timed after W warm-up steps."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth import CONFIGS
+    from synth.device import torch_dtype
+    from synth.make import draw_context_lens
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.config]
+    rng = np.random.default_rng(cfg.seed)
+    B, Hq, Hkv, D, PS = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    byte = cfg.kv_dtype in ("i8", "fp8")
+    src_t = cfg.q_dtype if byte else cfg.kv_dtype
+    n_req = 4 * B
+    prompts = np.concatenate([draw_context_lens(cfg, rng) for _ in range(4)])[:n_req]
+    new_tok = rng.integers(32, 257, size=n_req)
+    cap = int(prompts.max() + new_tok.max())
+    max_blocks = -(-cap // PS)
+    dev = "cuda"
+    shape = (cfg.num_pages, Hkv, PS, D)
+    if byte:
+        pools = [torch.zeros(shape, dtype=torch.uint8, device=dev).view(torch_dtype(cfg.kv_dtype)) for _ in range(2)]
+        scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+    else:
+        pools = [torch.zeros(shape, dtype=torch_dtype(cfg.kv_dtype), device=dev) for _ in range(2)]
+        scales = [None, None]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    rows_prompt = [torch.randn((int(prompts.max()), Hkv, D), generator=gen, device=dev).to(torch_dtype(src_t))
+                   for _ in range(2)]
+    rows_new = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch_dtype(src_t)) for _ in range(2)]
+    q = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch_dtype(cfg.q_dtype))
+    out = torch.empty_like(q)
+    bt_max = torch.zeros((B, max_blocks), dtype=torch.int32, device=dev)
+    ctx_max = torch.zeros(B, dtype=torch.int32, device=dev)
+    a = pkv.decode_args(q, pools[0], pools[1], bt_max, ctx_max, cfg.scale, max_context_len=cap,
+                        k_scale=scales[0], v_scale=scales[1], out=out)
+    ws = pkv.alloc_workspace(a, q.device)
+    ctr = pkv.alloc_merge_counters(a, q.device)
+    stream = torch.cuda.current_stream()
+    e_kv = 1 if byte else 2
+    pool = pkv.KVPool(cfg.num_pages, PS, initial_free_order=rng.permutation(cfg.num_pages))
+    sch = pkv.Scheduler(pool, B, pkv.CONTINUOUS)
+    for i in range(n_req):
+        sch.submit(i, int(prompts[i]), int(new_tok[i]), 0)
+    host_s = [0.0]
+    evs = []
+
+    def one_step(timed_events):
+        t_h = time.perf_counter()
+        s = sch.step()
+        for sid in s.admitted:
+            pages = np.asarray(pool.pages(int(sid)), dtype=np.int64)
+            n = int(prompts[int(sid)])
+            t = np.arange(n, dtype=np.int64)
+            slots = torch.from_numpy(pages[t // PS] * PS + t % PS).to(dev, non_blocking=True)
+            pkv.write_kv(rows_prompt[0][:n], rows_prompt[1][:n], slots, pools[0], pools[1],
+                         k_scale=scales[0], v_scale=scales[1])
+        n = len(s.seq_ids)
+        if n == 0:
+            host_s[0] += time.perf_counter() - t_h
+            return 0, 0
+        slots = torch.from_numpy(s.new_slots).to(dev, non_blocking=True)
+        pkv.write_kv(rows_new[0][:n], rows_new[1][:n], slots, pools[0], pools[1],
+                     k_scale=scales[0], v_scale=scales[1])
+        bt, ctx = pool.block_tables([int(x) for x in s.seq_ids], max_blocks)
+        bt_d = torch.from_numpy(bt).to(dev, non_blocking=True)
+        ctx_d = torch.from_numpy(ctx).to(dev, non_blocking=True)
+        host_s[0] += time.perf_counter() - t_h
+        if timed_events is not None:
+            ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            ev[0].record(stream)
+        pkv.paged_attn_decode(q[:n], pools[0], pools[1], bt_d, ctx_d, cfg.scale, max_context_len=cap,
+                              out=out[:n], k_scale=scales[0], v_scale=scales[1], workspace=ws,
+                              merge_counters=ctr)
+        if timed_events is not None:
+            ev[1].record(stream)
+            timed_events.append(ev)
+        kv = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * e_kv + (int(ctx.sum()) * Hkv * 8 if byte else 0)
+        return n, kv
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    host_s[0] = 0.0
+    t0 = time.perf_counter()
+    tokens = kv_bytes = 0
+    for _ in range(args.steps):
+        n, kv = one_step(evs)
+        tokens += n
+        kv_bytes += kv
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dec_ms = float(sum(e[0].elapsed_time(e[1]) for e in evs))
+    st_ = sch.stats()
+    sch.close()
+    pool.close()
+    print(json.dumps({
+        "metric": "continuous-batching decode loop, sequences decoded per second (one layer)",
+        "value": round(tokens / el, 1), "unit": "sequence-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(el * 1e3 / args.steps, 4), "higher_is_better": True,
+        "dtype": cfg.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"serve_{cfg.name}", "max_batch": B, "requests": n_req,
+                   "prompt_law": cfg.lens_kind, "new_tokens": "uniform 32..256", "page_size": PS},
+        "avg_batch": round(tokens / args.steps, 2),
+        "decode_kernel_us_per_step": round(dec_ms * 1e3 / max(len(evs), 1), 2),
+        "decode_kv_GBps": round(kv_bytes / (dec_ms * 1e-3) / 1e9, 1) if dec_ms else None,
+        "host_us_per_step": round(host_s[0] * 1e6 / args.steps, 1),
+        "scheduler": {"now": st_["now"], "finished": st_["finished"], "waiting": st_["waiting"]},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -347,6 +472,9 @@ def main():
         return
     if args.op == "append":
         bench_append(args)
+        return
+    if args.op == "serve":
+        bench_serve(args)
         return
 
     import paged_kv_cache_266_amd as pkv

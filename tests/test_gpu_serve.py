@@ -1,0 +1,142 @@
+"""GPU check of the continuous-batching loop (needs a gfx950 GPU).
+
+The native scheduler runs a stream of requests over a page pool.  Every step
+writes the admitted prompts' K/V and each running sequence's new token's K/V
+at the slots the scheduler hands out (pkv_write_kv, quantising f16 / bf16 rows
+into int8 / fp8 pools), then decodes the mixed batch over the block tables the
+pool builds.  Each step's output is compared with the fp64 oracle over a host
+mirror of the pools (written with the oracle's scatter and quantiser), so the
+slots, the block tables, the context lengths and the page reuse of retired
+sequences are all checked through decode.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import compare, note, small_config
+from synth.device import torch_dtype
+from synth.make import Case, _to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_266_amd as pkv
+
+    pkv.lib()
+    yield
+
+
+def _dev16(bits, name, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch_dtype(name)).to(dev)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,qd,kvd,PS,policy,max_batch", [
+    (32, 8, 128, "bf16", "bf16", 16, "continuous", 4),
+    (16, 16, 128, "f16", "i8", 16, "continuous", 5),
+    (8, 2, 64, "bf16", "fp8", 64, "static", 3),
+    (4, 2, 64, "f16", "f16", 16, "continuous", 1),
+])
+def test_serving_loop_decodes_every_step(Hq, Hkv, D, qd, kvd, PS, policy, max_batch):
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    note(f"serve: Hq {Hq} Hkv {Hkv} D {D} {qd}/{kvd} PS {PS} {policy} max_batch {max_batch}")
+    rng = np.random.default_rng(2026)
+    n_req, max_prompt, max_new = 12, 150, 12
+    cap = max_prompt + max_new
+    num_pages = max_batch * -(-cap // PS) + 3
+    cfg = small_config(Hq, Hkv, D, qd, kvd, PS, (cap,) * max_batch, num_pages=num_pages)
+    byte = kvd in ("i8", "fp8")
+    dev = "cuda"
+    shape = (num_pages, Hkv, PS, D)
+    if byte:
+        pools = [torch.zeros(shape, dtype=torch.uint8, device=dev).view(torch_dtype(kvd)) for _ in range(2)]
+        scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+        host = [np.zeros(shape, dtype=np.int8 if kvd == "i8" else np.uint8) for _ in range(2)]
+        host_s = [np.zeros(shape[:3], dtype=np.float32) for _ in range(2)]
+    else:
+        pools = [torch.zeros(shape, dtype=torch_dtype(kvd), device=dev) for _ in range(2)]
+        scales = [None, None]
+        host = [np.zeros(shape, dtype=np.uint16) for _ in range(2)]
+        host_s = [None, None]
+    src = qd if byte else kvd
+
+    def write(slots):
+        n = len(slots)
+        if n == 0:
+            return
+        rows = [_to_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32), src) for _ in range(2)]
+        pkv.write_kv(_dev16(rows[0], src, dev), _dev16(rows[1], src, dev),
+                     torch.from_numpy(np.asarray(slots, dtype=np.int64)).to(dev), pools[0], pools[1],
+                     k_scale=scales[0], v_scale=scales[1])
+        for w in range(2):
+            if byte:
+                exact = (rows[w].view(np.float16).astype(np.float32) if src == "f16"
+                         else (rows[w].astype(np.uint32) << 16).view(np.float32))
+                codes, s = oracle.quantize_rows(exact, kvd)
+                oracle.scatter_rows(host[w], slots, codes)
+                oracle.scatter_rows(host_s[w][..., None], slots, s[..., None])
+            else:
+                oracle.scatter_rows(host[w], slots, rows[w])
+
+    pol = pkv.CONTINUOUS if policy == "continuous" else pkv.STATIC
+    steps = decoded = 0
+    with pkv.KVPool(num_pages, PS, initial_free_order=rng.permutation(num_pages)) as pool:
+        sch = pkv.Scheduler(pool, max_batch, pol)
+        arrive = 0
+        prompts = {}
+        for i in range(n_req):
+            arrive += int(rng.integers(0, 3))
+            prompts[100 + i] = int(rng.integers(0, max_prompt + 1))
+            sch.submit(100 + i, prompts[100 + i], int(rng.integers(1, max_new + 1)), arrive)
+        while not sch.done():
+            s = sch.step()
+            steps += 1
+            for sid in s.admitted:
+                pages = pool.pages(int(sid))
+                write([pages[t // PS] * PS + t % PS for t in range(prompts[int(sid)])])
+            n = len(s.seq_ids)
+            if n == 0:
+                continue
+            write(list(s.new_slots))
+            bt, ctx = pool.block_tables([int(x) for x in s.seq_ids], cfg.max_blocks)
+            assert np.array_equal(ctx, s.context_lens)
+            q_bits = _to_bits(rng.standard_normal((n, Hq, D)).astype(np.float32), qd)
+            out = pkv.paged_attn_decode(_dev16(q_bits, qd, dev), pools[0], pools[1],
+                                        torch.from_numpy(bt).to(dev), torch.from_numpy(ctx).to(dev),
+                                        cfg.scale, max_context_len=cap, k_scale=scales[0], v_scale=scales[1])
+            torch.cuda.synchronize()
+            step_cfg = small_config(Hq, Hkv, D, qd, kvd, PS, (cap,) * n, num_pages=num_pages)
+            case = Case(cfg=step_cfg, seed=0, context_lens=ctx, free_order=np.arange(num_pages, dtype=np.int32),
+                        block_tables=bt, q_bits=q_bits, used_pages=np.arange(num_pages, dtype=np.int32),
+                        page_index=np.arange(num_pages, dtype=np.int32), k_pages=host[0], v_pages=host[1],
+                        k_scale=host_s[0], v_scale=host_s[1], scale=cfg.scale)
+            compare(case, out, f"step {s.step} batch {n}") if s.step % 5 == 0 else _quiet(case, out)
+            decoded += n
+        st_ = sch.stats()
+        assert st_["finished"] == n_req and pool.free_page_count() == num_pages
+        sch.close()
+    # the device pools hold the host mirror's bytes
+    for w in range(2):
+        got = pools[w].view(torch.uint8 if byte else torch.int16).cpu().numpy()
+        assert np.array_equal(got.view(host[w].dtype), host[w])
+        if byte:
+            assert np.array_equal(scales[w].cpu().numpy().view(np.uint32), host_s[w].view(np.uint32))
+    note(f"  {steps} steps, {decoded} sequence-steps decoded")
+
+
+def _quiet(case, out):
+    from gpu_helpers import TOL, to_f64
+
+    err = np.abs(to_f64(out) - oracle.paged_decode(case)).max()
+    assert err <= TOL[case.cfg.kv_dtype], f"max |gpu - oracle| = {err}"
