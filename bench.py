@@ -329,6 +329,8 @@ def bench_serve(args) -> None:
     4 x batch requests whose prompt lengths follow the workload's length law
     and which generate 32..256 tokens each (uniform), all arrived at step 0,
     at most `batch` running.  K steps are timed after W warm-up steps."""
+    import ctypes
+
     import numpy as np
     import torch
 
@@ -372,43 +374,124 @@ def bench_serve(args) -> None:
     ws = pkv.alloc_workspace(a, q.device)
     ctr = pkv.alloc_merge_counters(a, q.device)
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
     e_kv = 1 if byte else 2
     pool = pkv.KVPool(cfg.num_pages, PS, initial_free_order=rng.permutation(cfg.num_pages))
     sch = pkv.Scheduler(pool, B, pkv.CONTINUOUS)
     for i in range(n_req):
         sch.submit(i, int(prompts[i]), int(new_tok[i]), 0)
+
+    # per-step host -> device staging: [new slots int64 | context lens | block
+    # tables], a ring of pinned host buffers, one copy per step; a buffer is
+    # reused once its copy has completed (polled, not waited on: a blocking
+    # event wait costs a wake-up of ~0.2 ms here)
+    from paged_kv_cache_266_amd._lib import DTYPE_CODES, WriteArgs, check, lib
+
+    L = lib()
+    # host -> device copies straight through the HIP runtime torch has loaded
+    # (torch's copy_ of a slice of pinned memory looks the pointer up first)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    H2D = 1
+
+    def h2d(dst_ptr, src_ptr, nbytes):
+        if hip.hipMemcpyAsync(dst_ptr, src_ptr, nbytes, H2D, sh) != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
+
+    words = 3 * B + B * max_blocks
+    RING = 16
+    pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
+    pin_np = [t.numpy() for t in pin]
+    copied = [None] * RING
+    stage = torch.empty(words, dtype=torch.int32, device=dev)
+    slots_dev = stage[:2 * B].view(torch.int64)
+    wa = WriteArgs()
+    wa.k_new, wa.v_new = rows_new[0].data_ptr(), rows_new[1].data_ptr()
+    wa.slots = slots_dev.data_ptr()
+    wa.k_pool, wa.v_pool = pools[0].data_ptr(), pools[1].data_ptr()
+    wa.k_scale = 0 if scales[0] is None else scales[0].data_ptr()
+    wa.v_scale = 0 if scales[1] is None else scales[1].data_ptr()
+    wa.num_kv_heads, wa.head_dim, wa.page_size, wa.num_pages = Hkv, D, PS, cfg.num_pages
+    wa.kv_dtype, wa.src_dtype = DTYPE_CODES[cfg.kv_dtype], DTYPE_CODES[src_t]
+    a.workspace = 0 if ws is None else ws.data_ptr()
+    a.workspace_bytes = 0 if ws is None else ws.numel()
+    a.merge_counters = 0 if ctr is None else ctr.data_ptr()
+    a.merge_counter_bytes = 0 if ctr is None else 4 * ctr.numel()
+    a.context_lens = stage[2 * B:].data_ptr()
+    a.block_tables = stage[3 * B:].data_ptr()
+    # admitted prompts' slots: pinned host buffers in turn, one copy each
+    max_prompt_slots = B * int(prompts.max())
+    ppin = [torch.empty(max_prompt_slots, dtype=torch.int64, pin_memory=True) for _ in range(RING)]
+    ppin_np = [t.numpy() for t in ppin]
+    pcopied = [None] * RING
+    pstage = torch.empty(max_prompt_slots, dtype=torch.int64, device=dev)
     host_s = [0.0]
+    parts = {"sched_step": 0.0, "prompts": 0.0, "poll": 0.0, "tables": 0.0, "launch": 0.0}
     evs = []
+    k = [0]
 
     def one_step(timed_events):
         t_h = time.perf_counter()
         s = sch.step()
-        for sid in s.admitted:
-            pages = np.asarray(pool.pages(int(sid)), dtype=np.int64)
-            n = int(prompts[int(sid)])
-            t = np.arange(n, dtype=np.int64)
-            slots = torch.from_numpy(pages[t // PS] * PS + t % PS).to(dev, non_blocking=True)
-            pkv.write_kv(rows_prompt[0][:n], rows_prompt[1][:n], slots, pools[0], pools[1],
-                         k_scale=scales[0], v_scale=scales[1])
+        t_1 = time.perf_counter()
+        parts["sched_step"] += t_1 - t_h
+        if len(s.admitted):
+            i = k[0] % RING
+            while pcopied[i] is not None and not pcopied[i].query():
+                time.sleep(2e-5)
+            off, spans = 0, []
+            for sid in s.admitted:
+                pages = np.asarray(pool.pages(int(sid)), dtype=np.int64)
+                n = int(prompts[int(sid)])
+                t = np.arange(n, dtype=np.int64)
+                ppin_np[i][off:off + n] = pages[t // PS] * PS + t % PS
+                spans.append((off, n))
+                off += n
+            h2d(pstage.data_ptr(), ppin[i].data_ptr(), off * 8)
+            pcopied[i] = torch.cuda.Event()
+            pcopied[i].record(stream)
+            for off, n in spans:
+                pkv.write_kv(rows_prompt[0][:n], rows_prompt[1][:n], pstage[off:off + n], pools[0], pools[1],
+                             k_scale=scales[0], v_scale=scales[1])
+        t_2 = time.perf_counter()
+        parts["prompts"] += t_2 - t_1
         n = len(s.seq_ids)
         if n == 0:
             host_s[0] += time.perf_counter() - t_h
             return 0, 0
-        slots = torch.from_numpy(s.new_slots).to(dev, non_blocking=True)
-        pkv.write_kv(rows_new[0][:n], rows_new[1][:n], slots, pools[0], pools[1],
-                     k_scale=scales[0], v_scale=scales[1])
-        bt, ctx = pool.block_tables([int(x) for x in s.seq_ids], max_blocks)
-        bt_d = torch.from_numpy(bt).to(dev, non_blocking=True)
-        ctx_d = torch.from_numpy(ctx).to(dev, non_blocking=True)
-        host_s[0] += time.perf_counter() - t_h
+        i = k[0] % RING
+        k[0] += 1
+        while copied[i] is not None and not copied[i].query():
+            time.sleep(2e-5)                 # the copy from this buffer RING steps ago
+        t_p = time.perf_counter()
+        parts["poll"] += t_p - t_2
+        t_2 = t_p
+        h = pin_np[i]
+        h[:2 * B].view(np.int64)[:n] = s.new_slots
+        bt, ctx = sch.batch_tables(max_blocks, h[3 * B:3 * B + n * max_blocks].reshape(n, max_blocks),
+                                   h[2 * B:2 * B + n])
+        t_3 = time.perf_counter()
+        parts["tables"] += t_3 - t_2
         if timed_events is not None:
-            ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record(stream)
-        pkv.paged_attn_decode(q[:n], pools[0], pools[1], bt_d, ctx_d, cfg.scale, max_context_len=cap,
-                              out=out[:n], k_scale=scales[0], v_scale=scales[1], workspace=ws,
-                              merge_counters=ctr)
+        h2d(stage.data_ptr(), pin[i].data_ptr(), words * 4)
+        copied[i] = torch.cuda.Event()
+        copied[i].record(stream)
         if timed_events is not None:
             ev[1].record(stream)
+        wa.n = n
+        check(L.pkv_write_kv(ctypes.byref(wa), sh), "write_kv")
+        a.batch, a.max_blocks = n, max_blocks
+        t_4 = time.perf_counter()
+        parts["launch"] += t_4 - t_3
+        host_s[0] += t_4 - t_h
+        if timed_events is not None:
+            ev[2].record(stream)
+        check(L.pkv_paged_attn_decode(ctypes.byref(a), sh), "decode")
+        if timed_events is not None:
+            ev[3].record(stream)
             timed_events.append(ev)
         kv = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * e_kv + (int(ctx.sum()) * Hkv * 8 if byte else 0)
         return n, kv
@@ -417,6 +500,8 @@ def bench_serve(args) -> None:
         one_step(None)
     torch.cuda.synchronize()
     host_s[0] = 0.0
+    for key in parts:
+        parts[key] = 0.0
     t0 = time.perf_counter()
     tokens = kv_bytes = 0
     for _ in range(args.steps):
@@ -425,7 +510,11 @@ def bench_serve(args) -> None:
         kv_bytes += kv
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    dec_ms = float(sum(e[0].elapsed_time(e[1]) for e in evs))
+    dec_ms = float(sum(e[2].elapsed_time(e[3]) for e in evs))
+    gpu_parts = {"copy": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
+                 "write_kv": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
+                 "decode": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3,
+                 "between_steps": float(np.mean([a_[3].elapsed_time(b_[0]) for a_, b_ in zip(evs, evs[1:])])) * 1e3}
     st_ = sch.stats()
     sch.close()
     pool.close()
@@ -440,6 +529,8 @@ def bench_serve(args) -> None:
         "decode_kernel_us_per_step": round(dec_ms * 1e3 / max(len(evs), 1), 2),
         "decode_kv_GBps": round(kv_bytes / (dec_ms * 1e-3) / 1e9, 1) if dec_ms else None,
         "host_us_per_step": round(host_s[0] * 1e6 / args.steps, 1),
+        "host_us_breakdown": {key: round(v * 1e6 / args.steps, 1) for key, v in parts.items()},
+        "gpu_us_breakdown": {key: round(v, 1) for key, v in gpu_parts.items()},
         "scheduler": {"now": st_["now"], "finished": st_["finished"], "waiting": st_["waiting"]},
     }), flush=True)
 

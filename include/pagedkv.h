@@ -423,6 +423,15 @@ pkv_status pkv_sched_step(pkv_sched *sched, int32_t capacity, int64_t *seq_ids,
                           int64_t *new_slots, int32_t *context_lens, int64_t *admitted,
                           int64_t *retired, pkv_sched_step_out *out);
 
+/* Block tables and context lengths of the batch the last step ran (the
+ * running sequences, in batch order), as pkv_build_block_tables writes them:
+ * block_tables_out (host, [capacity][max_blocks]), context_lens_out (host,
+ * [capacity]); *n_out receives the batch size.  INVALID_ARG if capacity is
+ * below it or a sequence has more than max_blocks pages. */
+pkv_status pkv_sched_batch_tables(const pkv_sched *sched, int32_t capacity, int32_t max_blocks,
+                                  int32_t *block_tables_out, int32_t *context_lens_out,
+                                  int32_t *n_out);
+
 typedef struct pkv_sched_stats {
     int64_t now;                /* the clock                                         */
     int32_t waiting;            /* queued requests                                   */

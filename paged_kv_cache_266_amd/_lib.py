@@ -36,7 +36,7 @@ EXPORTED = [
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
     "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
     "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
-    "pkv_sched_get_stats",
+    "pkv_sched_get_stats", "pkv_sched_batch_tables",
 ]
 
 PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC = 0, 1
@@ -202,6 +202,8 @@ def _declare(L):
     L.pkv_sched_finish.argtypes = [vp, i64]
     L.pkv_sched_step.restype = ci
     L.pkv_sched_step.argtypes = [vp, i32, P(i64), P(i64), P(i32), P(i64), P(i64), P(SchedStepOut)]
+    L.pkv_sched_batch_tables.restype = ci
+    L.pkv_sched_batch_tables.argtypes = [vp, i32, i32, P(i32), P(i32), P(i32)]
     L.pkv_sched_get_stats.restype = ci
     L.pkv_sched_get_stats.argtypes = [vp, P(SchedStats)]
     return L

@@ -220,6 +220,25 @@ extern "C" pkv_status pkv_sched_step(pkv_sched *s, int32_t capacity, int64_t *se
     return PKV_OK;
 }
 
+extern "C" pkv_status pkv_sched_batch_tables(const pkv_sched *s, int32_t capacity, int32_t max_blocks,
+                                             int32_t *block_tables_out, int32_t *context_lens_out,
+                                             int32_t *n_out)
+{
+    pkv::clear_error();
+    if (!s || !n_out || (!s->running.empty() && (!block_tables_out || !context_lens_out)))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_sched_batch_tables: null argument");
+    const int32_t n = (int32_t)s->running.size();
+    if (capacity < n)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_sched_batch_tables: capacity below the batch size");
+    *n_out = n;
+    if (n == 0)
+        return PKV_OK;
+    std::vector<int64_t> ids((size_t)n);
+    for (int32_t i = 0; i < n; ++i)
+        ids[(size_t)i] = s->running[(size_t)i].id;
+    return pkv_build_block_tables(s->pool, ids.data(), n, max_blocks, block_tables_out, context_lens_out);
+}
+
 extern "C" pkv_status pkv_sched_get_stats(const pkv_sched *s, pkv_sched_stats *out)
 {
     pkv::clear_error();

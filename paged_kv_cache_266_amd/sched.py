@@ -42,6 +42,11 @@ class Scheduler:
         self._lens = np.empty(n, np.int32)
         self._adm = np.empty(n, np.int64)
         self._ret = np.empty(n, np.int64)
+        p64, p32 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+        self._out = SchedStepOut()
+        self._argv = (self._ids.ctypes.data_as(p64), self._slots.ctypes.data_as(p64),
+                      self._lens.ctypes.data_as(p32), self._adm.ctypes.data_as(p64),
+                      self._ret.ctypes.data_as(p64), ctypes.byref(self._out))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -67,16 +72,27 @@ class Scheduler:
         check(lib().pkv_sched_finish(self._h, seq_id), "finish")
 
     def step(self) -> Step:
-        out = SchedStepOut()
-        p64 = ctypes.POINTER(ctypes.c_int64)
-        check(lib().pkv_sched_step(self._h, self.max_batch, self._ids.ctypes.data_as(p64),
-                                   self._slots.ctypes.data_as(p64),
-                                   self._lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                   self._adm.ctypes.data_as(p64), self._ret.ctypes.data_as(p64),
-                                   ctypes.byref(out)), "step")
+        check(lib().pkv_sched_step(self._h, self.max_batch, *self._argv), "step")
+        out = self._out
         n = out.n_running
         return Step(out.step, self._ids[:n].copy(), self._slots[:n].copy(), self._lens[:n].copy(),
                     self._adm[:out.n_admitted].copy(), self._ret[:out.n_retired].copy())
+
+    def batch_tables(self, max_blocks: int, block_tables=None, context_lens=None):
+        """Block tables [n][max_blocks] and context lengths [n] (int32) of the
+        last step's batch.  Writes into the given arrays (host memory of at
+        least max_batch rows, e.g. pinned staging) when passed; returns the
+        filled views."""
+        p32 = ctypes.POINTER(ctypes.c_int32)
+        bt = np.empty((self.max_batch, max_blocks), np.int32) if block_tables is None else block_tables
+        lens = np.empty(self.max_batch, np.int32) if context_lens is None else context_lens
+        if bt.dtype != np.int32 or lens.dtype != np.int32 or not bt.flags.c_contiguous or bt.shape[1] != max_blocks:
+            raise ValueError("block_tables must be C-contiguous int32 [rows][max_blocks], context_lens int32")
+        cap = min(bt.shape[0], lens.shape[0])
+        n = ctypes.c_int32()
+        check(lib().pkv_sched_batch_tables(self._h, cap, max_blocks, bt.ctypes.data_as(p32),
+                                           lens.ctypes.data_as(p32), ctypes.byref(n)), "batch_tables")
+        return bt[:n.value], lens[:n.value]
 
     def stats(self) -> dict:
         st = SchedStats()

@@ -124,3 +124,23 @@ def test_step_reports_oom_when_the_pool_is_shared():
         s = sch.step()
         assert list(s.seq_ids) == [1]
         sch.close()
+
+
+def test_batch_tables_match_the_pool():
+    with pkv.KVPool(64, 4, initial_free_order=np.random.default_rng(3).permutation(64)) as pool:
+        sch = pkv.Scheduler(pool, 3)
+        for i, (p, n) in enumerate([(5, 3), (0, 4), (9, 2), (2, 2)]):
+            sch.submit(i, p, n, 0)
+        while not sch.done():
+            s = sch.step()
+            bt, lens = sch.batch_tables(8)
+            want_bt, want_lens = pool.block_tables([int(x) for x in s.seq_ids], 8) if len(s.seq_ids) else (bt, lens)
+            assert len(lens) == len(s.seq_ids)
+            assert np.array_equal(lens, s.context_lens)
+            if len(s.seq_ids):
+                assert np.array_equal(bt, want_bt) and np.array_equal(lens, want_lens)
+        with pytest.raises(pkv.PagedKVError):
+            sch.submit(9, 40, 1, 0)
+            sch.step()
+            sch.batch_tables(8, np.empty((0, 8), np.int32), np.empty(0, np.int32))
+        sch.close()
