@@ -668,17 +668,21 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     bool any_bad = false;
     const size_t page_stride = (size_t)Hkv * S::TILE_BYTES;
     // Physical pages of the cursor's tile (-1: none / outside the pool); the
-    // table is read at a clamped index so the lookup needs no branch.
+    // table is read at a clamped index so the lookup needs no branch.  True
+    // if a page the tile needs lies outside the pool (its segment's output
+    // becomes NaN once the tile is the current one).
     auto pages_of = [&](const Cursor &c, int (&ph)[PPT]) {
         const int32_t *bt = p.block_tables + (size_t)min(c.b, p.batch - 1) * p.max_blocks;
+        bool bad = false;
 #pragma unroll
         for (int pg = 0; pg < PPT; ++pg) {
             const int v = bt[min(c.k * PPT + pg, p.max_blocks - 1)];
             const bool exists = c.k * kTileTokens + pg * PS < c.n;
             const bool inside = (unsigned)v < (unsigned)p.num_pages;
-            any_bad = any_bad || (exists && !inside);
+            bad = bad || (exists && !inside);
             ph[pg] = exists && inside ? v : -1;
         }
+        return bad;
     };
     auto tile_rem = [&](const Cursor &c) { return min(kTileTokens, c.n - c.k * kTileTokens); };
     auto own_page = [&](const int (&ph)[PPT]) {
@@ -765,7 +769,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // has been used -- across segment boundaries too.
     const int lane_off = r * S::ROW + S::CB * j;
     int ph_cur[PPT], ph_nxt[PPT];
-    pages_of(cur, ph_cur);
+    bool bad_cur = pages_of(cur, ph_cur), bad_nxt = false;
     TileAddr<S> ka, va;
     ka.set((const char *)p.k_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
     va.set((const char *)p.v_pool + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), r);
@@ -800,8 +804,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const bool last_in_range = t + 1 == hi;
         const Cursor nxt = last_in_range ? cur : advance(cur);
         const bool seg_end = last_in_range || nxt.k == 0;
+        any_bad = any_bad || bad_cur;
+        bad_nxt = false;
         if (!last_in_range)
-            pages_of(nxt, ph_nxt);
+            bad_nxt = pages_of(nxt, ph_nxt);
         else
 #pragma unroll
             for (int pg = 0; pg < PPT; ++pg)
@@ -1029,7 +1035,505 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             ph_cur[pg] = ph_nxt[pg];
         ks_cur = ks_nxt;
         vs_cur = vs_nxt;
+        bad_cur = bad_nxt;
         cur = nxt;
+    }
+
+    if (p.fused) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int npend = __builtin_amdgcn_readfirstlane(s_npend);
+        for (int i = 0; i < npend; ++i)
+            settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),
+                                   __builtin_amdgcn_readfirstlane(s_pend[i][1]),
+                                   __builtin_amdgcn_readfirstlane(s_pend[i][2]), (int)w, lane);
+    }
+}
+
+// ---- fp8 KV on the matrix cores (head_dim 128) ---------------------------------
+//
+// The same walk over the batch's tiles as paged_decode_kernel, for E4M3 K/V,
+// with both contractions of a tile on the matrix cores
+// (v_mfma_f32_16x16x32_{bf16,f16}: D[16][16] += A[16][32] . B[32][16]; lane
+// l supplies A[l%16][8(l/16) + i] and B[8(l/16) + i][l%16], i < 8, and holds
+// D[4(l/16) + v][l%16], v < 4).  Lane l is (a, c) = (l/16, l%16).  With G
+// query heads per KV head only G of the 16 rows (or columns) carry data; the
+// vector unit, which in the vector kernel spends most of an fp8 tile on the
+// products and their reductions, is left with the E4M3 widening and the
+// softmax.
+//
+//  * q.k.  Lane (a, c) loads 16 bytes of K: dims 64s + 16a .. +16 of token
+//    16tb + c (chunk 2tb + s).  Each half (dims 64s + 16a + 8h .. +8) is
+//    widened exactly to q's type and is the B operand of dim step 2s + h; q
+//    (rows = heads) is the A operand, lane (a, c) holding
+//    q[head c][64s + 16a + 8h .. +8] -- the same dims at the same k index,
+//    so the contraction runs over all 128 dims in a permuted order.  Scores
+//    land in lane (a, c), register v: head 4a + v, token 16tb + c; the K
+//    scale of that token multiplies them.
+//  * p.V.  V keeps the row layout of the vector kernel's byte path: lane
+//    (a, c) holds dims 8c .. 8c+7 of token 4J + a (chunk J, 8 bytes).  For
+//    dim offset e and half H of the tile, A[m = c][k = 8a + i] =
+//    V[token 4(8H + i) + a][dim 8c + e] comes from byte e of chunks 8H .. 8H+7:
+//    one byte permute per two chunks and two dims, then one widening to a
+//    bf16 pair.  B[k][n] = p[head n][that token] times the token's V scale,
+//    rounded to bf16, comes from LDS; O^T[dim 8m + e][head n] accumulates in
+//    8 x 4 registers.  (p in bf16 carries a relative error of at most 2^-9
+//    per term, below the output's own rounding; an f16 q would need p times
+//    the V scale in f16, whose range that product can leave.)
+//  * The register ring, masking, online softmax and piece / merge handling
+//    are those of the vector kernel.
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (QT == BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }
+        (std::make_integer_sequence<int, N>{});
+}
+
+// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = fmaxf(x, dpp<0x128>(x));
+    x = fmaxf(x, dpp<0x124>(x));
+    x = fmaxf(x, dpp<0x122>(x));
+    x = fmaxf(x, dpp<0x121>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += dpp<0x128>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x122>(x);
+    x += dpp<0x121>(x);
+    return x;
+}
+
+// Eight E4M3 codes (bytes of w0, w1) widened exactly to 8 values of q's type.
+template <int QT>
+__device__ __forceinline__ u32x4 widen8(u32 w0, u32 w1)
+{
+    return u32x4{fp8_pair16<QT, false>(w0), fp8_pair16<QT, true>(w0), fp8_pair16<QT, false>(w1),
+                 fp8_pair16<QT, true>(w1)};
+}
+
+// K of one 64-token fp8 tile in the q.k operand layout: chunk I = 2tb + s
+// holds, for lane (a, c), the 16 bytes of dims 64s + 16a .. of token 16tb + c.
+template <int PS>
+struct Fp8KOperandTile {
+    static constexpr int ROW = 128, TILE_BYTES = PS * ROW, PPT = kTileTokens / PS;
+    const char *base[PPT];
+    int nblocks;   // token blocks (of 16) that hold this lane's token
+
+    __device__ __forceinline__ void set(const char *head, size_t page_stride, const int (&ph)[PPT], int rem, int c)
+    {
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg)
+            base[pg] = uniform_ptr(head + (size_t)(ph[pg] >= 0 ? ph[pg] : 0) * page_stride);
+        nblocks = rem > c ? (rem - c + 15) / 16 : 0;
+    }
+
+    template <int I>
+    __device__ __forceinline__ u32x4 load(int lane_off) const
+    {
+        constexpr int tb = I / 2, st = I % 2;
+        constexpr int pg = (16 * tb) / PS;
+        constexpr int chunk_off = ((16 * tb) % PS) * ROW + 64 * st;
+        const int voff = tb < nblocks ? lane_off : kOutOfRange;
+        return __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(base[pg], TILE_BYTES), voff, chunk_off,
+                                                     kStreamingLoad);
+    }
+};
+
+template <int PS, int G, int QT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void paged_decode_fp8_mfma_kernel(DecodeParams p)
+{
+    constexpr int D = 128;
+    using S = Shape<D, PS, G, QT, FP8>;
+    constexpr int PPT = S::PPT;
+    static_assert(S::R == 16 && S::TPI == 4 && S::EPL == 8 && S::CB == 8, "layout of the 128-dim fp8 tile");
+    static_assert(G <= 16, "one head per matrix row");
+
+    __shared__ float s_p[16 * 64];   // probabilities times V scales: [head][token % 4][token / 4]
+    __shared__ int s_pend[2][3];
+    __shared__ int s_npend;
+
+    const int lane = threadIdx.x;
+    const int a = lane / 16, c = lane % 16;
+    const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+    const long long NW = gridDim.x, w = blockIdx.x;
+
+    const long long T = (long long)batch_tiles(p, lane) * Hkv;
+    for (long long b = w; b < p.batch; b += NW) {
+        const int n = p.context_lens[b];
+        if (tiles_of(n, p.max_context_len) == 0) {
+            const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
+            u32 *o = reinterpret_cast<u32 *>(p.out) + (size_t)b * Hq * D / 2;
+            for (int i = lane; i < Hq * D / 2; i += 64)
+                o[i] = pack_out<QT>(fill, fill);
+        }
+    }
+    const long long NWe = NW < T ? NW : T;
+    if (w >= NWe)
+        return;
+    const long long lo = range_start(w, T, NWe), hi = range_start(w + 1, T, NWe);
+    if (w == 0 && lane == 0)
+        *p.ws_tag = p.tag;
+
+    struct Cursor {
+        int b, n, nt, g, k;
+        __device__ __forceinline__ void make_uniform()
+        {
+            b = __builtin_amdgcn_readfirstlane(b);
+            n = __builtin_amdgcn_readfirstlane(n);
+            nt = __builtin_amdgcn_readfirstlane(nt);
+            g = __builtin_amdgcn_readfirstlane(g);
+            k = __builtin_amdgcn_readfirstlane(k);
+        }
+    };
+    Cursor cur;
+    {
+        long long start;
+        locate(p, lo, lane, cur.b, start);
+        cur.n = p.context_lens[cur.b];
+        cur.nt = tiles_of(cur.n, p.max_context_len);
+        const long long off = lo - start;
+        cur.g = (int)(off / cur.nt);
+        cur.k = (int)(off % cur.nt);
+        cur.make_uniform();
+    }
+    auto advance = [&](const Cursor &x0) {
+        Cursor x = x0;
+        if (++x.k == x.nt) {
+            x.k = 0;
+            if (++x.g == Hkv) {
+                x.g = 0;
+                do {
+                    ++x.b;
+                    x.n = x.b < p.batch ? p.context_lens[x.b] : 0;
+                    x.nt = tiles_of(x.n, p.max_context_len);
+                } while (x.nt == 0 && x.b < p.batch);
+            }
+        }
+        x.make_uniform();
+        return x;
+    };
+
+    bool any_bad = false;
+    const size_t page_stride = (size_t)Hkv * S::TILE_BYTES;
+    auto pages_of = [&](const Cursor &x, int (&ph)[PPT]) {
+        const int32_t *bt = p.block_tables + (size_t)min(x.b, p.batch - 1) * p.max_blocks;
+        bool bad = false;
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg) {
+            const int v = bt[min(x.k * PPT + pg, p.max_blocks - 1)];
+            const bool exists = x.k * kTileTokens + pg * PS < x.n;
+            const bool inside = (unsigned)v < (unsigned)p.num_pages;
+            bad = bad || (exists && !inside);
+            ph[pg] = exists && inside ? v : -1;
+        }
+        return bad;
+    };
+    auto tile_rem = [&](const Cursor &x) { return min(kTileTokens, x.n - x.k * kTileTokens); };
+    // K and V scales of tokens 16tb + c of the cursor's tile (0 for a token
+    // that is not there)
+    auto scales_of = [&](const Cursor &x, const int (&ph)[PPT], float (&ks)[4], float (&vs)[4]) {
+        const int rem = x.n - x.k * kTileTokens;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int pg = (16 * tb) / PS;
+            const bool ok = ph[pg] >= 0 && 16 * tb + c < rem;
+            const size_t si = ok ? ((size_t)ph[pg] * Hkv + x.g) * PS + (16 * tb) % PS + c : 0;
+            const float kv = p.k_scale[si], vv = p.v_scale[si];
+            ks[tb] = ok ? kv : 0.0f;
+            vs[tb] = ok ? vv : 0.0f;
+        }
+    };
+
+    // q of the segment as the A operand of the four dim steps: lane (a, c)
+    // holds q[head c][64s + 16a + 8h .. +8] in qa[2s + h] (zero for c >= G)
+    u32x4 qa[4];
+    auto load_q = [&](const Cursor &x) {
+        const char *base = (const char *)p.q + (((size_t)x.b * Hq + (size_t)x.g * G + (c < G ? c : 0)) * D) * 2;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(base + (64 * (st / 2) + 16 * a + 8 * (st % 2)) * 2);
+            qa[st] = c < G ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    f32x4 acc[8];               // O^T[dim 8(4a + v) + e][head c] in acc[e][v]
+    float m_row[4], l_row[4];   // running max / this lane's sum for head 4a + v
+    auto reset_state = [&]() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            m_row[v] = -INFINITY;
+            l_row[v] = 0.0f;
+        }
+    };
+    // value of a per-head quantity held row-wise (head 4a + v in register v of
+    // row a) for the head of this lane's column, c
+    auto head_of_column = [&](const float (&row)[4]) {
+        float r = 1.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float x = lane_value(row[h % 4], 16 * (h / 4));
+            r = c == h ? x : r;
+        }
+        return r;
+    };
+
+    const int lane_off_k = c * S::ROW + 16 * a;
+    const int lane_off_v = a * S::ROW + 8 * c;
+    // Pages two tiles deep: the tile being computed, the next one (whose K
+    // and V are in flight) and the one after it (whose block-table entries
+    // are being read).
+    const char *k_head = (const char *)p.k_pool, *v_head = (const char *)p.v_pool;
+    int ph_cur[PPT], ph_nxt[PPT], ph_nx2[PPT];
+    bool bad_cur = pages_of(cur, ph_cur), bad_nxt = false, bad_nx2 = false;
+    Fp8KOperandTile<PS> ka;
+    TileAddr<S> va;
+    ka.set(k_head + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), c);
+    va.set(v_head + (size_t)cur.g * S::TILE_BYTES, page_stride, ph_cur, tile_rem(cur), a);
+    // K chunk I (16 bytes) in rk[I]; V chunks 2I, 2I + 1 (8 bytes each) in
+    // rv[I].  Each is refilled with the next tile's chunk as soon as it has
+    // been used, so both K and V are a whole tile ahead of the arithmetic.
+    u32x4 rk[8], rv[8];
+    static_for<8>([&](auto Ic) {
+        constexpr int I = decltype(Ic)::value;
+        rk[I] = ka.template load<I>(lane_off_k);
+    });
+    static_for<8>([&](auto Ic) {
+        constexpr int I = decltype(Ic)::value;
+        const u32x2 v0 = va.template load<2 * I>(lane_off_v);
+        const u32x2 v1 = va.template load<2 * I + 1>(lane_off_v);
+        rv[I] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    });
+    load_q(cur);
+    reset_state();
+    float ks_cur[4], vs_cur[4], ks_nxt[4], vs_nxt[4];
+    scales_of(cur, ph_cur, ks_cur, vs_cur);
+    bool piece_from_start = cur.k == 0;
+    if (lane == 0)
+        s_npend = 0;
+    Cursor nxt = lo + 1 < hi ? advance(cur) : cur;
+    if (lo + 1 < hi)
+        bad_nxt = pages_of(nxt, ph_nxt);
+    else
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg)
+            ph_nxt[pg] = -1;
+
+    for (long long t = lo; t < hi; ++t) {
+        if (cur.k == 0 && lane == 0)
+            p.seg_geo[cur.b * Hkv + cur.g] =
+                make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
+        const bool last_in_range = t + 1 == hi;
+        const bool has_nx2 = t + 2 < hi;
+        const Cursor nx2 = has_nx2 ? advance(nxt) : nxt;
+        const bool seg_end = last_in_range || nxt.k == 0;
+        any_bad = any_bad || bad_cur;
+        bad_nx2 = false;
+        if (has_nx2)
+            bad_nx2 = pages_of(nx2, ph_nx2);
+        else
+#pragma unroll
+            for (int pg = 0; pg < PPT; ++pg)
+                ph_nx2[pg] = -1;
+        // the next tile's addresses (nothing is read for a tile past the range)
+        ka.set(k_head + (size_t)nxt.g * S::TILE_BYTES, page_stride, ph_nxt, last_in_range ? 0 : tile_rem(nxt), c);
+        va.set(v_head + (size_t)nxt.g * S::TILE_BYTES, page_stride, ph_nxt, last_in_range ? 0 : tile_rem(nxt), a);
+        scales_of(nxt, ph_nxt, ks_nxt, vs_nxt);
+
+        // ---- q.k on the matrix cores; each K chunk's registers then take
+        // the next tile's K chunk
+        f32x4 sc[4];
+        static_for<4>([&](auto TBc) {
+            constexpr int TB = decltype(TBc)::value;
+            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+            static_for<2>([&](auto Sc) {
+                constexpr int ST = decltype(Sc)::value;
+                constexpr int I = 2 * TB + ST;
+                const u32x4 kc = rk[I];
+                x = mfma32<QT>(qa[2 * ST], widen8<QT>(kc[0], kc[1]), x);
+                x = mfma32<QT>(qa[2 * ST + 1], widen8<QT>(kc[2], kc[3]), x);
+                rk[I] = ka.template load<I>(lane_off_k);
+            });
+            sc[TB] = x;
+        });
+
+        // ---- online softmax (log2 domain): lane (a, c), register v holds
+        // head 4a + v, token 16tb + c
+        const int rem = cur.n - cur.k * kTileTokens;
+        float alpha_row[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float x = 16 * tb + c < rem ? sc[tb][v] * ks_cur[tb] * p.scale_log2 : -INFINITY;
+                sc[tb][v] = x;
+                mx = fmaxf(mx, x);
+            }
+            const float m_new = fmaxf(m_row[v], row_max16(mx));
+            alpha_row[v] = __builtin_amdgcn_exp2f(m_row[v] - m_new);
+            float ls = 0.0f;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float e = __builtin_amdgcn_exp2f(sc[tb][v] - m_new);
+                sc[tb][v] = e;
+                ls += e;
+            }
+            l_row[v] = l_row[v] * alpha_row[v] + ls;
+            m_row[v] = m_new;
+        }
+        // probabilities times the V scale to LDS, [head][token % 4][token / 4]
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                s_p[(4 * a + v) * 64 + (c % 4) * 16 + 4 * tb + c / 4] = sc[tb][v] * vs_cur[tb];
+        const float alpha_c = head_of_column(alpha_row);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] *= alpha_c;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- p.V on the matrix cores, one half of the tile (32 tokens) at a time
+        static_for<2>([&](auto Hc) {
+            constexpr int H = decltype(Hc)::value;
+            const float *src = s_p + (c < G ? c : 0) * 64 + a * 16 + 8 * H;
+            const float4 p0 = *reinterpret_cast<const float4 *>(src);
+            const float4 p1 = *reinterpret_cast<const float4 *>(src + 4);
+            u32x4 bop = {pack_out<BF16>(p0.x, p0.y), pack_out<BF16>(p0.z, p0.w), pack_out<BF16>(p1.x, p1.y),
+                         pack_out<BF16>(p1.z, p1.w)};
+            if (c >= G)
+                bop = u32x4{0u, 0u, 0u, 0u};
+            // A operand of dim offset e: bf16 pairs (chunk 8H + 2q, chunk 8H + 2q + 1), q < 4
+            static_for<2>([&](auto Dc) {
+                constexpr int DW = decltype(Dc)::value;   // dword of the 8-byte chunks: dims 4DW .. 4DW+3
+                u32x4 aop[4];
+                static_for<4>([&](auto Qc) {
+                    constexpr int Q = decltype(Qc)::value;
+                    const u32x4 pr = rv[4 * H + Q];        // chunks 8H + 2Q (x, y), 8H + 2Q + 1 (z, w)
+                    // bytes (c0.k, c1.k, c0.k+1, c1.k+1) for k = 0 and k = 2
+                    const u32 b01 = __builtin_amdgcn_perm(pr[2 + DW], pr[DW], 0x05010400u);
+                    const u32 b23 = __builtin_amdgcn_perm(pr[2 + DW], pr[DW], 0x07030602u);
+                    aop[0][Q] = fp8_pair16<BF16, false>(b01);
+                    aop[1][Q] = fp8_pair16<BF16, true>(b01);
+                    aop[2][Q] = fp8_pair16<BF16, false>(b23);
+                    aop[3][Q] = fp8_pair16<BF16, true>(b23);
+                });
+                static_for<4>([&](auto Kc) {
+                    constexpr int K = decltype(Kc)::value;
+                    acc[4 * DW + K] = mfma32<BF16>(aop[K], bop, acc[4 * DW + K]);
+                });
+            });
+            static_for<4>([&](auto Jc) {
+                constexpr int I = 4 * H + decltype(Jc)::value;
+                const u32x2 v0 = va.template load<2 * I>(lane_off_v);
+                const u32x2 v1 = va.template load<2 * I + 1>(lane_off_v);
+                rv[I] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+            });
+        });
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- end of a piece
+        if (seg_end) {
+            const bool whole = piece_from_start && cur.k == cur.nt - 1;
+            const int seg = cur.b * Hkv + cur.g;
+            const float nan = __builtin_nanf("");
+            float l_tot[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                l_tot[v] = row_sum16(l_row[v]);
+            const float l_c = head_of_column(l_tot);
+            const float m_c = head_of_column(m_row);
+            if (c < G) {
+                if (whole) {
+                    const size_t unit = (size_t)cur.b * Hq + (size_t)cur.g * G + c;
+                    const float inv = any_bad ? nan : 1.0f / l_c;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const u32x4 o = {pack_out<QT>(acc[0][v] * inv, acc[1][v] * inv),
+                                         pack_out<QT>(acc[2][v] * inv, acc[3][v] * inv),
+                                         pack_out<QT>(acc[4][v] * inv, acc[5][v] * inv),
+                                         pack_out<QT>(acc[6][v] * inv, acc[7][v] * inv)};
+                        *reinterpret_cast<u32x4 *>(reinterpret_cast<u32 *>(p.out) + (unit * D + 8 * (4 * a + v)) / 2) = o;
+                    }
+                } else {
+                    const size_t slot = (size_t)seg + (size_t)w;
+                    float *po = uniform_fptr(p.part_o + slot * G * D);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int off = (c * D + 8 * (4 * a + v)) * 4;
+                        store_coherent4(po, G * D * 4, off,
+                                        any_bad ? make_float4(nan, nan, nan, nan)
+                                                : make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]));
+                        store_coherent4(po, G * D * 4, off + 16,
+                                        any_bad ? make_float4(nan, nan, nan, nan)
+                                                : make_float4(acc[4][v], acc[5][v], acc[6][v], acc[7][v]));
+                    }
+                    if (a == 0)
+                        store_coherent2(uniform_fptr(p.part_ml + slot * G * 2), G * 8, c * 8,
+                                        make_float2(m_c, any_bad ? nan : l_c));
+                }
+            }
+            if (!whole) {
+                const long long first = t - cur.k;
+                const int w0 = (int)owner_of(first, T, NWe);
+                const int w1 = (int)owner_of(first + cur.nt - 1, T, NWe);
+                if (lane == 0) {
+                    const int i = s_npend;
+                    s_pend[i][0] = seg;
+                    s_pend[i][1] = w0;
+                    s_pend[i][2] = w1 - w0 + 1;
+                    s_npend = i + 1;
+                }
+            }
+            reset_state();
+            any_bad = false;
+            piece_from_start = true;
+            if (!last_in_range)
+                load_q(nxt);   // behind the next tile's K loads already in flight
+        }
+
+#pragma unroll
+        for (int pg = 0; pg < PPT; ++pg) {
+            ph_cur[pg] = ph_nxt[pg];
+            ph_nxt[pg] = ph_nx2[pg];
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            ks_cur[tb] = ks_nxt[tb];
+            vs_cur[tb] = vs_nxt[tb];
+        }
+        bad_cur = bad_nxt;
+        bad_nxt = bad_nx2;
+        cur = nxt;
+        nxt = nx2;
     }
 
     if (p.fused) {
@@ -1365,8 +1869,10 @@ int launch_one(const DecodeParams &p, hipStream_t stream)
 {
     dim3 grid((unsigned)p.num_splits);
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    return (int)hipLaunchKernel((const void *)&paged_decode_kernel<D, PS, G, QT, KVT>, grid, dim3(64),
-                                args, 0, stream);
+    const void *fn = (const void *)&paged_decode_kernel<D, PS, G, QT, KVT>;
+    if constexpr (KVT == FP8 && D == 128)
+        fn = (const void *)&paged_decode_fp8_mfma_kernel<PS, G, QT>;   // fp8 at head_dim 128: matrix cores
+    return (int)hipLaunchKernel(fn, grid, dim3(64), args, 0, stream);
 }
 
 template <int D, int PS, int G>

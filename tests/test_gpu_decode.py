@@ -10,6 +10,7 @@ import itertools
 import numpy as np
 import pytest
 
+import oracle
 from gpu_helpers import compare, gpu_decode, note, small_config, to_f64
 from synth import CONFIGS, make_case
 from synth.configs import ORDER
@@ -93,6 +94,51 @@ def test_poisoned_tails_do_not_leak():
         assert np.isfinite(to_f64(b)).all()
         assert torch_equal_bits(a.cpu(), b.cpu())
         compare(poisoned, b, name + " poisoned")
+
+
+@pytest.mark.parametrize("Hq,Hkv,qd,PS", [(32, 8, "bf16", 64), (16, 16, "f16", 16), (8, 1, "bf16", 16)])
+def test_poisoned_tails_do_not_leak_fp8(Hq, Hkv, qd, PS):
+    """E4M3 NaN codes (and NaN scales) in every slot past each sequence's
+    end: the output is finite and bitwise equal to the clean cache's."""
+    lens = (1, 15, 16, 17, 63, 64, 65, 200, 1000)
+    cfg = small_config(Hq, Hkv, 128, qd, "fp8", PS, lens)
+    note(f"[poison fp8] Hq={Hq} Hkv={Hkv} q={qd} PS={PS}")
+    clean = make_case(cfg, seed=31)
+    poisoned = make_case(cfg, seed=31, poison=True)
+    a = gpu_decode(clean)
+    b = gpu_decode(poisoned)
+    assert np.isfinite(to_f64(b)).all()
+    assert torch_equal_bits(a.cpu(), b.cpu())
+    compare(poisoned, b, "fp8 poisoned")
+
+
+@pytest.mark.parametrize("qd,kvd,PS", [("bf16", "bf16", 16), ("bf16", "bf16", 64), ("f16", "i8", 16),
+                                       ("bf16", "fp8", 16), ("f16", "fp8", 64)])
+def test_out_of_pool_block_table_entry_gives_nan_for_that_sequence_only(qd, kvd, PS):
+    """A block-table entry the sequence needs that lies outside the pool
+    (in its first tile, or in a middle one) makes that sequence's output NaN
+    -- every head, since all KV heads read the page -- and leaves every other
+    sequence equal to the oracle, however the tiles are split over waves
+    (a bad first tile right after another segment in the same wave's range
+    included)."""
+    import dataclasses
+
+    lens = (200, 130, 64, 300, 90)
+    cfg = small_config(32, 8, 128, qd, kvd, PS, lens)
+    note(f"[out-of-pool] q={qd} kv={kvd} PS={PS}")
+    clean = make_case(cfg, seed=55)
+    bt = clean.block_tables.copy()
+    bt[1, 0] = cfg.num_pages + 5            # first tile of sequence 1
+    bt[3, (128 + 10) // PS] = -7            # a middle tile of sequence 3
+    bad = dataclasses.replace(clean, block_tables=bt)
+    ref = oracle.paged_decode(clean)
+    good = [0, 2, 4]
+    from gpu_helpers import TOL
+    for splits in (0, 1, 2, 3, 7, 40):
+        g = to_f64(gpu_decode(bad, num_splits=splits))
+        assert np.isnan(g[1]).all() and np.isnan(g[3]).all(), splits
+        assert np.isfinite(g[good]).all(), splits
+        assert np.abs(g[good] - ref[good]).max() <= TOL[kvd], splits
 
 
 def test_page_permutation_invariance_bitwise():
