@@ -85,6 +85,14 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def decode_kernel_name(workload: str) -> str:
+    from synth import CONFIGS
+
+    cfg = CONFIGS[workload]
+    return "paged_decode_fp8_mfma_kernel" if cfg.kv_dtype == "fp8" and cfg.head_dim == 128 \
+        else "paged_decode_kernel"
+
+
 def _counter_rows(path, counter):
     import csv
 
@@ -102,12 +110,13 @@ def _per_dispatch(rows, match):
 
 
 def summarize_counters(workload: str, files, copy_bytes: int) -> dict:
-    """HBM bytes per launch of paged_decode_kernel from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each divided by what the same counter
-    reads per byte for a plain device copy of copy_bytes bytes."""
+    """HBM bytes per launch of the decode kernel (paged_decode_kernel, or
+    paged_decode_fp8_mfma_kernel) from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each divided by what the same counter reads per byte for a
+    plain device copy of copy_bytes bytes."""
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = files
-    fetch = _per_dispatch(_counter_rows(fetch_csv, "FETCH_SIZE"), "paged_decode_kernel")
-    write = _per_dispatch(_counter_rows(write_csv, "WRITE_SIZE"), "paged_decode_kernel")
+    fetch = _per_dispatch(_counter_rows(fetch_csv, "FETCH_SIZE"), "paged_decode_")
+    write = _per_dispatch(_counter_rows(write_csv, "WRITE_SIZE"), "paged_decode_")
     # the copy kernel is the largest dispatch of the calibration run
     cf = max(_per_dispatch(_counter_rows(cfetch_csv, "FETCH_SIZE"), ""))
     cw = max(_per_dispatch(_counter_rows(cwrite_csv, "WRITE_SIZE"), ""))
@@ -117,7 +126,7 @@ def summarize_counters(workload: str, files, copy_bytes: int) -> dict:
     write_b = sum(write) / len(write) * 1024 / w_factor
     return {
         "workload": workload,
-        "kernel": "paged_decode_kernel",
+        "kernel": decode_kernel_name(workload),
         "source_digest": source_digest(),
         "dispatches": {"fetch": len(fetch), "write": len(write)},
         "fetch_kib_per_dispatch": round(sum(fetch) / len(fetch), 1),
@@ -695,7 +704,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel",
+            "kernel": decode_kernel_name(cfg.name),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
