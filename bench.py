@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="distinct layer buffers cycled through (0 = enough for >= 1 GB of KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="time a plain 2 GiB device copy and a read-only reduction (HBM reference)")
     ap.add_argument("--op", choices=["decode", "append", "serve"], default="decode",
                     help="decode: the decode step (default); append: write every token of the workload "
                          "into the pools with pkv_write_kv (quantising f16/bf16 rows for int8/fp8 pools); "
@@ -151,6 +153,33 @@ def copy_calibration(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def stream_reference(mib: int, reps: int = 20) -> None:
+    """What plain streams reach on this GPU, as a practical reference for the
+    HBM roofline: a device-to-device copy (bytes read + written) and a
+    read-only reduction (torch's sum of a bf16 buffer into fp32), timed with
+    HIP events over `reps` launches each."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * n),
+                            ("read (sum)", lambda: torch.sum(src, dtype=torch.float32), n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"us": round(us, 1), "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+    print(json.dumps({"stream_reference_bytes": n, "results": res}), flush=True)
 
 
 def cpu_baseline(case, min_seconds: float, got, tol: float):
@@ -569,6 +598,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(COPY_CALIBRATION_MIB)
+        return
+    if args.stream_reference:
+        stream_reference(2048)
         return
     if args.op == "append":
         bench_append(args)
