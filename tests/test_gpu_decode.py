@@ -141,6 +141,33 @@ def test_out_of_pool_block_table_entry_gives_nan_for_that_sequence_only(qd, kvd,
         assert np.abs(g[good] - ref[good]).max() <= TOL[kvd], splits
 
 
+@pytest.mark.parametrize("kvd,qd", [("bf16", "bf16"), ("fp8", "bf16")])
+def test_one_million_token_context(kvd, qd):
+    """One sequence of 2^20 tokens (8x the 128k workload) spread over the
+    whole grid and merged, next to a 1-token sequence."""
+    n = 1 << 20
+    cfg = small_config(8, 1, 128, qd, kvd, 64, (n, 1), num_pages=(n // 64) + 8)
+    note(f"[max context] {n} tokens, kv={kvd}")
+    case = make_case(cfg, seed=77)
+    out = gpu_decode(case)
+    compare(case, out, "1M tokens")
+
+
+def test_four_thousand_sequences():
+    """A batch of 4096 short ragged sequences (lengths 0..130): more segments
+    than waves, many empty ones, every wave crossing many segment ends."""
+    rng = np.random.default_rng(8)
+    lens = tuple(int(x) for x in rng.integers(0, 131, size=4096))
+    cfg = small_config(8, 2, 64, "f16", "f16", 16, lens)
+    note("[max batch] 4096 sequences")
+    case = make_case(cfg, seed=9)
+    for splits in (0, 1024, 5000):
+        out = gpu_decode(case, num_splits=splits)
+        compare(case, out, f"4096 seqs, splits={splits}")
+        g = to_f64(out)
+        assert (g[np.asarray(lens) == 0] == 0).all()
+
+
 def test_page_permutation_invariance_bitwise():
     cfg = CONFIGS["llama3_8b_gqa"]
     note("[perm] llama3_8b_gqa, 2 re-permutations")

@@ -15,7 +15,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 from oracle.kvsize import kv_bytes, kv_bytes_per_token
-from oracle.pool_model import (OutOfPages, PagePoolModel, SequenceExists,
+from oracle.pool_model import (OutOfPages, PagePoolModel, SequenceExists, SharedLastPage,
                                UnknownSequence, pages_needed)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -164,7 +164,6 @@ def test_long_context_config_is_about_2p1_gb_per_layer():
 # shared last page.
 
 def test_fork_and_copy_on_write_trace():
-    from oracle.pool_model import SharedLastPage
 
     m = PagePoolModel(16, 6)                      # free list [0..5], pop from the end
     assert m.allocate(0, 20)[:2] == [5 * 16, 5 * 16 + 1]
@@ -213,7 +212,6 @@ fork_ops = st.lists(st.tuples(st.sampled_from(["alloc", "append", "append_cow", 
 @settings(max_examples=300, deadline=None)
 @given(st.sampled_from([1, 4, 16]), st.integers(1, 24), fork_ops)
 def test_owner_counts_hold_after_any_operation_sequence(ps, num_pages, seq):
-    from oracle.pool_model import SharedLastPage
 
     m = PagePoolModel(ps, num_pages)
     for op, sid, n, other in seq:
