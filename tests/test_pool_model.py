@@ -195,6 +195,19 @@ def test_fork_and_copy_on_write_trace():
     assert m.refcount == {}
 
 
+def test_copy_page_is_taken_before_overflow_pages():
+    """An append that both copies a shared, partly filled last page and
+    overflows: the copy gets the first page popped, the overflow the next."""
+    m = PagePoolModel(4, 10)                      # pops 9, 8, 7, ...
+    m.allocate(0, 6)                              # pages [9, 8], 2 tokens in page 8
+    m.fork(0, 1)
+    slots, copy = m.append_tokens_cow(1, 5)       # tokens 6..10
+    assert copy == (8, 7)
+    assert m.page_table[1] == [9, 7, 6] and m.page_table[0] == [9, 8]
+    assert slots == [7 * 4 + 2, 7 * 4 + 3, 6 * 4 + 0, 6 * 4 + 1, 6 * 4 + 2]
+    assert m.refcount == {9: 2, 8: 1, 7: 1, 6: 1}
+
+
 def test_copy_on_write_is_all_or_nothing():
     m = PagePoolModel(4, 3)
     m.allocate(0, 6)                               # pages [2, 1], one free
