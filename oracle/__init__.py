@@ -7,7 +7,9 @@ with the HIP library (``paged_kv_cache_266_amd``) and never imports it.
 Contents:
 
 * ``oracle.c`` -- the paged decode definition in plain C, fp64, OpenMP over
-  (sequence, query head) units; loaded here through ctypes.
+  (sequence, query head) units, and chunked prefill (causal context
+  attention of a chunk of new tokens over the same paged cache); loaded
+  here through ctypes.
 * ``brute.py`` -- pure-Python contiguous attention (no pages) for tiny inputs.
 * ``pool_model.py`` -- the free-list page allocator, as a Python model.
 * ``sched_model.py`` -- the continuous-batching step driver over that pool.
@@ -71,6 +73,9 @@ def load(path: str):
     L.oracle_quantize_rows.argtypes = [ci, ci, ci, ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
     L.oracle_quantize_rows.restype = ci
+    L.oracle_paged_prefill.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, ci, vp, vp, f32p, f32p, i32p, ci, ci,
+                                       i32p, ci, i32p, ctypes.c_float, f64p, ci]
+    L.oracle_paged_prefill.restype = ci
     return L
 
 
@@ -172,6 +177,29 @@ def paged_decode_split(case, partition_tokens: int, n_threads: Optional[int] = N
         raise OracleError(f"oracle_paged_decode_split returned {rc}")
     del keep
     return (out, m, l, o) if with_stats else out
+
+
+def paged_prefill(case, q_bits: np.ndarray, q_start: np.ndarray,
+                  n_threads: Optional[int] = None) -> np.ndarray:
+    """fp64 chunked-prefill attention ``[n_q][Hq][D]``: the query rows
+    ``q_start[b] .. q_start[b+1]-1`` of ``q_bits`` are sequence b's last
+    tokens, each attending causally to the paged cache of ``case`` (whose
+    context lengths include them)."""
+    c = case.cfg
+    q_bits = np.ascontiguousarray(q_bits)
+    q_start = np.ascontiguousarray(q_start, dtype=np.int32)
+    n_q = int(q_start[-1])
+    if q_bits.shape != (n_q, c.num_q_heads, c.head_dim) or q_start.shape != (c.batch + 1,):
+        raise OracleError("prefill: q / q_start shapes do not match the case")
+    out = np.empty((n_q, c.num_q_heads, c.head_dim), dtype=np.float64)
+    args, keep = _common_args(case, q_bits)
+    # _common_args' argument list, with q_start inserted after q
+    args = args[:7] + [_ptr(q_start, ctypes.c_int32)] + args[7:]
+    rc = lib().oracle_paged_prefill(*args, _ptr(out, ctypes.c_double), n_threads or default_threads())
+    if rc != 0:
+        raise OracleError(f"oracle_paged_prefill returned {rc}")
+    del keep
+    return out
 
 
 def scatter_rows(pool: np.ndarray, slots: np.ndarray, src: np.ndarray) -> None:

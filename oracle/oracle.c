@@ -144,11 +144,11 @@ static double kv_elem(const problem *p, int which, long row, int g, int slot, in
     return x;
 }
 
-/* Scores s_t = scale * <q_bh, k_t> for t in [t0, t1); returns 0 or ORC_BAD_PAGE. */
-static int scores(const problem *p, int b, int h, int t0, int t1, double *s)
+/* Scores s_t = scale * <q, k_t> for the query vector at element offset qoff
+ * of q, against the keys of kv head g of sequence b, t in [t0, t1); returns
+ * 0 or ORC_BAD_PAGE. */
+static int scores_q(const problem *p, size_t qoff, int g, int b, int t0, int t1, double *s)
 {
-    int g = h / (p->Hq / p->Hkv);
-    size_t qoff = ((size_t)b * p->Hq + h) * p->D;
     for (int t = t0; t < t1; ++t) {
         long row = page_row(p, b, t);
         if (row < 0)
@@ -161,12 +161,19 @@ static int scores(const problem *p, int b, int h, int t0, int t1, double *s)
     return ORC_OK;
 }
 
-/* Softmax-weighted sum over tokens [t0, t1) against a given max M:
- * writes acc[d] = sum_t exp(s_t - M) * v_t[d] and returns sum_t exp(s_t - M). */
-static double weighted_v(const problem *p, int b, int h, int t0, int t1,
-                         const double *s, double M, double *acc)
+/* Decode: the query of sequence b, head h is row b of q [B][Hq][D]. */
+static int scores(const problem *p, int b, int h, int t0, int t1, double *s)
 {
     int g = h / (p->Hq / p->Hkv);
+    size_t qoff = ((size_t)b * p->Hq + h) * p->D;
+    return scores_q(p, qoff, g, b, t0, t1, s);
+}
+
+/* Softmax-weighted sum over tokens [t0, t1) against a given max M:
+ * writes acc[d] = sum_t exp(s_t - M) * v_t[d] and returns sum_t exp(s_t - M). */
+static double weighted_v_g(const problem *p, int g, int b, int t0, int t1,
+                           const double *s, double M, double *acc)
+{
     for (int d = 0; d < p->D; ++d)
         acc[d] = 0.0;
     double Z = 0.0;
@@ -178,6 +185,13 @@ static double weighted_v(const problem *p, int b, int h, int t0, int t1,
             acc[d] += w * kv_elem(p, 1, row, g, t % p->PS, d);
     }
     return Z;
+}
+
+static double weighted_v(const problem *p, int b, int h, int t0, int t1,
+                         const double *s, double M, double *acc)
+{
+    int g = h / (p->Hq / p->Hkv);
+    return weighted_v_g(p, g, b, t0, t1, s, M, acc);
 }
 
 static int check(const problem *p)
@@ -352,6 +366,77 @@ int oracle_paged_decode_split(int B, int Hq, int Hkv, int D, int PS,
             }
         }
         free(m); free(l); free(ok); free(s);
+    }
+    return status;
+}
+
+/*
+ * Chunked prefill (context attention over the paged cache).  Sequence b's
+ * new tokens are query rows q_start[b] .. q_start[b+1]-1 of q [n_q][Hq][D]:
+ * the last nq = q_start[b+1] - q_start[b] of the context_lens[b] tokens its
+ * cache holds (their own K/V included).  Query i sits at position
+ * context_lens[b] - nq + i and attends causally to keys 0 .. that position,
+ * with the decode path's scaled-dot-product softmax.  out[n_q][Hq][D].
+ */
+int oracle_paged_prefill(int B, int Hq, int Hkv, int D, int PS,
+                         int q_dtype, const void *q, const int32_t *q_start,
+                         int kv_dtype, const void *k_pages, const void *v_pages,
+                         const float *k_scale, const float *v_scale,
+                         const int32_t *page_index, int num_pages, int n_host_pages,
+                         const int32_t *block_tables, int max_blocks,
+                         const int32_t *context_lens, float scale,
+                         double *out, int n_threads)
+{
+    problem p = {B, Hq, Hkv, D, PS, q_dtype, kv_dtype, q, k_pages, v_pages,
+                 k_scale, v_scale, page_index, num_pages, n_host_pages,
+                 block_tables, max_blocks, context_lens, (double)scale};
+    int rc = check(&p);
+    if (rc)
+        return rc;
+    if (!q_start || q_start[0] != 0)
+        return ORC_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        int nq = q_start[b + 1] - q_start[b];
+        if (nq < 0 || nq > context_lens[b])
+            return ORC_BAD_ARG;
+    }
+    int status = ORC_OK;
+    long units = (long)B * Hq;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
+    for (long u = 0; u < units; ++u) {
+        int b = (int)(u / Hq), h = (int)(u % Hq);
+        int g = h / (Hq / Hkv);
+        int n = context_lens[b], nq = q_start[b + 1] - q_start[b];
+        double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !acc) {
+#pragma omp atomic write
+            status = ORC_NO_MEM;
+            free(s);
+            free(acc);
+            continue;
+        }
+        for (int i = 0; i < nq; ++i) {
+            long row = q_start[b] + i;
+            int pos = n - nq + i;                 /* keys 0 .. pos */
+            double *o = out + ((size_t)row * Hq + h) * D;
+            if (scores_q(&p, ((size_t)row * Hq + h) * D, g, b, 0, pos + 1, s) != ORC_OK) {
+#pragma omp atomic write
+                status = ORC_BAD_PAGE;
+                for (int d = 0; d < D; ++d)
+                    o[d] = NAN;
+                continue;
+            }
+            double M = s[0];
+            for (int t = 1; t <= pos; ++t)
+                if (s[t] > M)
+                    M = s[t];
+            double Z = weighted_v_g(&p, g, b, 0, pos + 1, s, M, acc);
+            for (int d = 0; d < D; ++d)
+                o[d] = acc[d] / Z;
+        }
+        free(s);
+        free(acc);
     }
     return status;
 }

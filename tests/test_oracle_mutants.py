@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_prefill as prefill
 import test_oracle_quant as quant
 
 MUTANTS = {
@@ -43,6 +44,13 @@ MUTANTS = {
                           "static int scaled_kv(int dtype) { return dtype == ORC_I8; }"),
     "split_merge_missing_rescale": ("L += l[k] * exp(m[k] - M);", "L += l[k];"),
     "split_partition_max_wrong": ("m[k] = mk;", "m[k] = 0.0;"),
+    "prefill_position_off_by_one": ("int pos = n - nq + i;", "int pos = n - nq + i - 1;"),
+    "prefill_not_causal": ("double Z = weighted_v_g(&p, g, b, 0, pos + 1, s, M, acc);",
+                           "double Z = weighted_v_g(&p, g, b, 0, pos + 1, s, M, acc);\n"
+                           "            if (pos + 1 < n) { (void)scores_q(&p, ((size_t)row * Hq + h) * D, g, b, 0, n, s);"
+                           " M = s[0]; for (int t = 1; t < n; ++t) if (s[t] > M) M = s[t];"
+                           " Z = weighted_v_g(&p, g, b, 0, n, s, M, acc); }"),
+    "prefill_query_row_of_wrong_sequence": ("long row = q_start[b] + i;", "long row = q_start[b] + (nq - 1 - i);"),
 }
 
 PIN_SUITE = [
@@ -58,6 +66,11 @@ PIN_SUITE = [
     lambda: quant.test_quantiser_matches_generator_encoders("i8"),
     lambda: quant.test_quantiser_matches_generator_encoders("fp8"),
     quant.test_int8_ties_round_to_even,
+    *[(lambda s=s: prefill.test_prefill_matches_pure_python_causal_attention(s)) for s in pins.TINY_SHAPES[:3]],
+    lambda: prefill.test_last_query_of_a_chunk_is_a_decode_step(pins.TINY_SHAPES[0]),
+    prefill.test_causality_later_keys_do_not_matter,
+    prefill.test_first_token_of_a_sequence_returns_its_value,
+    prefill.test_a_query_depends_on_its_position_not_on_its_chunk,
     quant.test_fp8_encode_round_trips_every_finite_code,
     quant.test_fp8_encode_ties_and_saturation,
 ]
