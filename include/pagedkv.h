@@ -354,6 +354,54 @@ typedef struct pkv_copy_args {
 pkv_status pkv_copy_pages(const pkv_copy_args *args, void *stream);
 
 /* ===================================================================== *
+ * Device: chunked prefill (context attention) over the paged cache -- the
+ * chunked context of "TensorRT-LLM 深度实战", section 7.3: a long prompt is
+ * processed a chunk at a time, each chunk's queries attending to every
+ * earlier token of the sequence and causally to the chunk's own tokens, with
+ * the scaled-dot-product softmax of section 3.3.
+ * ===================================================================== */
+
+typedef struct pkv_prefill_args {
+    const void *q;              /* device [n_q][num_q_heads][head_dim], q_dtype: the
+                                   new tokens' queries, sequence after sequence       */
+    const void *k_pool;         /* device pools [num_pages][num_kv_heads][page_size]
+                                   [head_dim], kv_dtype (== q_dtype); the chunk's own
+                                   K/V already written (pkv_write_kv)                 */
+    const void *v_pool;
+    const int32_t *block_tables; /* device [batch][max_blocks], as for decode         */
+    const int32_t *q_start;     /* device [batch + 1]: sequence b's queries are rows
+                                   q_start[b] .. q_start[b+1]-1; q_start[0] = 0,
+                                   non-decreasing, q_start[batch] = n_q              */
+    const int32_t *context_lens; /* device [batch]: tokens in the cache, the chunk
+                                   included; query i of sequence b sits at position
+                                   context_lens[b] - nq_b + i and attends to keys
+                                   0 .. that position                                 */
+    void *out;                  /* device [n_q][num_q_heads][head_dim], q_dtype     */
+    int32_t batch;
+    int32_t n_q;                /* total query rows                                  */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;       /* num_q_heads / num_kv_heads in {1, 2, 4, 8}        */
+    int32_t head_dim;           /* 128                                               */
+    int32_t page_size;          /* 16 or 64                                          */
+    int32_t num_pages;
+    int32_t max_blocks;
+    int32_t max_context_len;    /* host bound on context_lens (<= max_blocks *
+                                   page_size)                                         */
+    int32_t max_q_len;          /* host bound on every sequence's chunk length       */
+    pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16                               */
+    pkv_dtype kv_dtype;         /* == q_dtype                                        */
+    float scale;
+} pkv_prefill_args;
+
+/* Chunked prefill attention; one launch, asynchronous on `stream`.  A
+ * sequence whose context length is negative, above max_context_len or shorter
+ * than its chunk gets NaN rows, as does any block of rows that needs a page
+ * outside the pool; rows of a sequence whose q_start entries are out of
+ * order or beyond n_q are not written.  UNSUPPORTED outside the instantiated
+ * shapes; INVALID_ARG for bad sizes or null pointers. */
+pkv_status pkv_paged_prefill(const pkv_prefill_args *args, void *stream);
+
+/* ===================================================================== *
  * Host: continuous-batching step driver over a pool.  One step follows
  * "TensorRT-LLM 深度实战", section 3.2: finished sequences leave the batch
  * and release their pages, waiting requests join while there is room (their

@@ -36,7 +36,7 @@ EXPORTED = [
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
     "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
     "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
-    "pkv_sched_get_stats", "pkv_sched_batch_tables",
+    "pkv_sched_get_stats", "pkv_sched_batch_tables", "pkv_paged_prefill",
 ]
 
 PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC = 0, 1
@@ -83,6 +83,19 @@ class CopyArgs(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("pairs", ctypes.c_void_p),
         ("n", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+    ]
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("q_start", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -202,6 +215,8 @@ def _declare(L):
     L.pkv_sched_finish.argtypes = [vp, i64]
     L.pkv_sched_step.restype = ci
     L.pkv_sched_step.argtypes = [vp, i32, P(i64), P(i64), P(i32), P(i64), P(i64), P(SchedStepOut)]
+    L.pkv_paged_prefill.restype = ci
+    L.pkv_paged_prefill.argtypes = [P(PrefillArgs), vp]
     L.pkv_sched_batch_tables.restype = ci
     L.pkv_sched_batch_tables.argtypes = [vp, i32, i32, P(i32), P(i32), P(i32)]
     L.pkv_sched_get_stats.restype = ci

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["decode.hip", "api.cpp", "pool.cpp", "sched.cpp"]
+SOURCES = ["decode.hip", "api.cpp", "pool.cpp", "sched.cpp", "prefill.hip", "prefill_api.cpp"]
 
 
 def hipcc() -> str:

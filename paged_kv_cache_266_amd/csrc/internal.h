@@ -99,6 +99,30 @@ struct CopyParams {
     int32_t tiles_per_page;   // set by the launcher
 };
 
+// Everything the chunked-prefill kernel reads; built from pkv_prefill_args.
+struct PrefillParams {
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *block_tables;
+    const int32_t *q_start;
+    const int32_t *context_lens;
+    void *out;
+    int32_t batch;
+    int32_t n_q;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_pages;
+    int32_t max_blocks;
+    int32_t max_context_len;
+    int32_t max_q_len;
+    int32_t q_dtype;
+    float scale_log2;     // softmax scale * log2(e)
+};
+
+bool prefill_instantiated(int head_dim, int page_size, int group, int q_dtype, int kv_dtype);
+int launch_prefill(const PrefillParams &p, int page_size, int group, void *stream);
+
 // 16-byte chunks of one page that one block of copy_pages_kernel copies
 constexpr int kCopyTileChunks = 1024;
 

@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional
 
-from ._lib import DTYPE_CODES, CopyArgs, DecodeArgs, WriteArgs, check, lib
+from ._lib import DTYPE_CODES, CopyArgs, DecodeArgs, PrefillArgs, WriteArgs, check, lib
 
 
 def _dtype_name(t) -> str:
@@ -149,6 +149,43 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         a.merge_counter_bytes = 0 if merge_counters is None else 4 * merge_counters.numel()
     check(lib().pkv_paged_attn_decode(ctypes.byref(a), _stream_handle(stream, q.device)),
           "paged_attn_decode")
+    return out
+
+
+def paged_prefill(q, k_pool, v_pool, block_tables, q_start, context_lens, scale: float, *,
+                  max_context_len: int, max_q_len: int, out=None, stream=None):
+    """Chunked prefill attention over a paged cache.
+
+    q [n_q][Hq][D] f16/bf16: sequence b's new tokens are rows
+    q_start[b] .. q_start[b+1]-1 (q_start int32 [B+1], device); the pools
+    (same type as q) already hold their K/V, and context_lens [B] counts them.
+    Query i of sequence b attends to keys 0 .. context_lens[b] - nq_b + i.
+    Returns out [n_q][Hq][D] in q's type."""
+    import torch
+
+    device = q.device
+    for t, n, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4),
+                     (block_tables, "block_tables", 2), (q_start, "q_start", 1),
+                     (context_lens, "context_lens", 1), (out, "out", 3)):
+        _check_tensor(t, n, device, nd)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or q_start.dtype != torch.int32:
+        raise TypeError("block_tables, q_start and context_lens must be int32")
+    n_q, Hq, D = q.shape
+    num_pages, Hkv, PS, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shape does not match q")
+    if out is None:
+        out = torch.empty_like(q)
+    a = PrefillArgs()
+    a.q, a.k_pool, a.v_pool = _ptr(q), _ptr(k_pool), _ptr(v_pool)
+    a.block_tables, a.q_start, a.context_lens, a.out = _ptr(block_tables), _ptr(q_start), _ptr(context_lens), _ptr(out)
+    a.batch, a.n_q, a.num_q_heads, a.num_kv_heads, a.head_dim = context_lens.shape[0], n_q, Hq, Hkv, D
+    a.page_size, a.num_pages, a.max_blocks = PS, num_pages, block_tables.shape[1]
+    a.max_context_len, a.max_q_len = int(max_context_len), int(max_q_len)
+    a.q_dtype = DTYPE_CODES[_dtype_name(q)]
+    a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
+    a.scale = float(scale)
+    check(lib().pkv_paged_prefill(ctypes.byref(a), _stream_handle(stream, device)), "paged_prefill")
     return out
 
 

@@ -1,0 +1,141 @@
+"""GPU parity of the chunked-prefill kernel (needs a gfx950 GPU).
+
+Each sequence's last nq tokens are the chunk: their K/V are in the paged
+cache (the generator's layout), their queries are new rows, and each query
+attends causally.  Every output row is compared with the fp64 oracle's
+chunked prefill; the large case compares the first and last rows of every
+chunk (the oracle, which recomputes each row from scratch, would take
+minutes for all of them), exploiting that a row depends only on keys up to
+its position."""
+
+import dataclasses
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, note, small_config, to_f64
+from synth import make_case
+from synth.device import torch_dtype, upload
+from synth.make import _to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_266_amd as pkv
+
+    pkv.lib()
+    yield
+
+
+def queries(cfg, chunks, seed):
+    rng = np.random.default_rng(seed)
+    n_q = int(sum(chunks))
+    q = rng.standard_normal((n_q, cfg.num_q_heads, cfg.head_dim)).astype(np.float32)
+    return _to_bits(q, cfg.q_dtype), np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+
+
+def gpu_prefill(case, q_bits, q_start, dev=None, max_q_len=None, context_lens=None):
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    cfg = case.cfg
+    dev = dev or upload(case, "cuda")
+    q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch_dtype(cfg.q_dtype)).cuda()
+    qs = torch.from_numpy(q_start).cuda()
+    ctx = dev.context_lens if context_lens is None else torch.from_numpy(context_lens).cuda()
+    mq = int(np.diff(q_start).max()) if max_q_len is None else max_q_len
+    out = pkv.paged_prefill(q, dev.k_pool, dev.v_pool, dev.block_tables, qs, ctx, case.scale,
+                            max_context_len=cfg.max_context_len, max_q_len=max(mq, 1))
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+def check(case, got, ref, label):
+    err = np.abs(got - ref)
+    tol = TOL[case.cfg.kv_dtype]
+    note(f"  {label}: max|err| {err.max():.3e} (tol {tol})")
+    assert np.isfinite(got).all(), label
+    assert err.max() <= tol, f"{label}: {err.max()} > {tol}"
+
+
+LENS = (1, 63, 64, 65, 300, 777)
+CHUNKS = (1, 63, 20, 65, 100, 130)
+
+
+@pytest.mark.parametrize("PS,G,qd", list(itertools.product((16, 64), (1, 2, 4, 8), ("f16", "bf16"))))
+def test_prefill_every_instantiation(PS, G, qd):
+    """Ragged chunks: a whole 1-token sequence, a whole 63-token one, parts
+    of longer ones, chunks spanning several query blocks (64/G tokens each)
+    and key tiles."""
+    Hkv = 2
+    cfg = small_config(G * Hkv, Hkv, 128, qd, qd, PS, LENS)
+    note(f"[prefill] PS={PS} G={G} q={qd}")
+    case = make_case(cfg, seed=300 + PS + G)
+    qb, qs = queries(cfg, CHUNKS, seed=PS + G)
+    got = gpu_prefill(case, qb, qs)
+    ref = oracle.paged_prefill(case, qb, qs)
+    check(case, got, ref, "all rows")
+
+
+def test_prefill_empty_chunks_and_invalid_lengths():
+    """A sequence with no new tokens is skipped; a context length shorter
+    than the chunk gives NaN rows for that sequence only."""
+    cfg = small_config(8, 2, 128, "bf16", "bf16", 16, (40, 90, 33))
+    case = make_case(cfg, seed=5)
+    qb, qs = queries(cfg, (0, 30, 10), seed=2)
+    got = gpu_prefill(case, qb, qs)
+    ref = oracle.paged_prefill(case, qb, qs)
+    check(case, got, ref, "empty chunk")
+    bad_ctx = case.context_lens.copy()
+    bad_ctx[2] = 5                                  # shorter than its 10-token chunk
+    got = gpu_prefill(case, qb, qs, context_lens=bad_ctx)
+    assert np.isnan(got[qs[2]:qs[3]]).all()
+    assert np.abs(got[qs[1]:qs[2]] - ref[qs[1]:qs[2]]).max() <= TOL["bf16"]
+
+
+def test_prefill_out_of_pool_page_gives_nan_rows():
+    cfg = small_config(8, 2, 128, "f16", "f16", 16, (100, 100))
+    case = make_case(cfg, seed=6)
+    qb, qs = queries(cfg, (40, 40), seed=3)
+    ref = oracle.paged_prefill(case, qb, qs)
+    bt = case.block_tables.copy()
+    bt[1, 2] = cfg.num_pages + 3                    # keys 32..47 of sequence 1
+    got = gpu_prefill(dataclasses.replace(case, block_tables=bt), qb, qs)
+    assert np.isnan(got[qs[1]:qs[2]]).all()
+    check(case, got[qs[0]:qs[1]], ref[qs[0]:qs[1]], "other sequence")
+
+
+@pytest.mark.parametrize("G,qd", [(4, "bf16"), (1, "f16")])
+def test_prefill_large_chunks_sampled_rows(G, qd):
+    """16 sequences with 512-token chunks after contexts of up to 3.5k tokens
+    (the chunked-context step of a long prompt): the first and last 8 rows of
+    every chunk against the oracle, computed as 8-row chunks at the same
+    positions."""
+    rng = np.random.default_rng(11)
+    chunk = 512
+    lens = tuple(int(x) for x in rng.integers(chunk, 4097, size=16))
+    Hkv = 8 if G == 4 else 16
+    cfg = small_config(G * Hkv, Hkv, 128, qd, qd, 64, lens)
+    case = make_case(cfg, seed=12)
+    qb, qs = queries(cfg, (chunk,) * len(lens), seed=13)
+    note(f"[prefill large] G={G} q={qd} chunks 16 x {chunk}")
+    got = gpu_prefill(case, qb, qs)
+    last = np.concatenate([qb[qs[b + 1] - 8:qs[b + 1]] for b in range(len(lens))])
+    qs8 = np.arange(0, 8 * len(lens) + 1, 8, dtype=np.int32)
+    ref_last = oracle.paged_prefill(case, last, qs8)
+    got_last = np.concatenate([got[qs[b + 1] - 8:qs[b + 1]] for b in range(len(lens))])
+    check(case, got_last, ref_last, "last 8 rows")
+    first = np.concatenate([qb[qs[b]:qs[b] + 8] for b in range(len(lens))])
+    early = dataclasses.replace(case, context_lens=(case.context_lens - (chunk - 8)).astype(np.int32))
+    ref_first = oracle.paged_prefill(early, first, qs8)
+    got_first = np.concatenate([got[qs[b]:qs[b] + 8] for b in range(len(lens))])
+    check(case, got_first, ref_first, "first 8 rows")
