@@ -47,11 +47,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-reference", action="store_true",
                     help="time a plain 2 GiB device copy and a read-only reduction (HBM reference)")
-    ap.add_argument("--op", choices=["decode", "append", "serve"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "serve", "prefill"], default="decode",
                     help="decode: the decode step (default); append: write every token of the workload "
                          "into the pools with pkv_write_kv (quantising f16/bf16 rows for int8/fp8 pools); "
                          "serve: the continuous-batching loop (scheduler step, K/V appends, decode of the "
-                         "mixed batch) over a backlog of requests of the workload's shape")
+                         "mixed batch) over a backlog of requests of the workload's shape; prefill: one "
+                         "chunked-prefill step (a 512-token chunk per sequence) of the workload's shape")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -573,6 +574,113 @@ def bench_serve(args) -> None:
     }), flush=True)
 
 
+PEAK_MFMA_TFLOPS_16BIT = 2500.0   # MI355X dense bf16 / f16
+
+
+def bench_prefill(args) -> None:
+    """One chunked-prefill step: every sequence of the workload processes a
+    chunk of 512 new tokens at the end of its context (lengths from the
+    workload's law, at least 512), 16-bit K/V.  FLOPs counted causally:
+    4 * head_dim per (query row, query head, visible key).  The cpu_baseline
+    leg runs the fp64 oracle on the last 8 rows of the first 4 chunks (its
+    first pass is also the parity check of those rows)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from synth import CONFIGS, make_case
+    from synth.configs import get_config
+    from synth.device import torch_dtype, upload
+    from synth.make import _to_bits, draw_context_lens
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    base = CONFIGS[args.config]
+    if base.kv_dtype not in ("f16", "bf16") or base.head_dim != 128:
+        raise SystemExit("prefill: 16-bit K/V at head_dim 128 only")
+    chunk = 512
+    rng = np.random.default_rng(base.seed)
+    lens = np.maximum(draw_context_lens(base, rng), chunk).astype(np.int32)
+    cfg = get_config(base.name, lens_kind="fixed", lens_args=tuple(int(x) for x in lens))
+    case = make_case(cfg)
+    dev = upload(case, "cuda")
+    B, Hq, D = cfg.batch, cfg.num_q_heads, cfg.head_dim
+    qrng = np.random.default_rng(cfg.seed + 1)
+    q_bits = _to_bits(qrng.standard_normal((B * chunk, Hq, D)).astype(np.float32), cfg.q_dtype)
+    q = torch.from_numpy(q_bits.view(np.int16)).view(torch_dtype(cfg.q_dtype)).cuda()
+    q_start = np.arange(0, B * chunk + 1, chunk, dtype=np.int32)
+    qs = torch.from_numpy(q_start).cuda()
+    out = torch.empty_like(q)
+
+    def step():
+        pkv.paged_prefill(q, dev.k_pool, dev.v_pool, dev.block_tables, qs, dev.context_lens, case.scale,
+                          max_context_len=cfg.max_context_len, max_q_len=chunk, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    tol = {"f16": 4e-3, "bf16": 1.6e-2}[cfg.kv_dtype]
+    parity, baseline = {"ok": None, "note": "not checked: --no-cpu-baseline"}, None
+    if not args.no_cpu_baseline:
+        import dataclasses
+
+        import oracle
+
+        nb, rows = 4, 8
+        sub = dataclasses.replace(case, cfg=get_config(cfg.name, batch=nb, lens_kind="fixed",
+                                                       lens_args=tuple(int(x) for x in lens[:nb])),
+                                  context_lens=case.context_lens[:nb], block_tables=case.block_tables[:nb])
+        sel = np.concatenate([np.arange(q_start[b + 1] - rows, q_start[b + 1]) for b in range(nb)])
+        qs8 = np.arange(0, nb * rows + 1, rows, dtype=np.int32)
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        ref = oracle.paged_prefill(sub, q_bits[sel], qs8, n_threads=threads)
+        el = time.perf_counter() - t0
+        err = float(np.abs(got[sel] - ref).max())
+        parity = {"rows_checked": int(sel.size), "max_abs_err": err, "tol": tol, "ok": bool(err <= tol)}
+        flops_s = 4.0 * D * Hq * sum(int(lens[b]) - rows + i + 1 for b in range(nb) for i in range(rows))
+        baseline = {"value": round(flops_s / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                    "sample": f"the last {rows} rows of the first {nb} chunks, {el:.2f} s"}
+    # causal FLOPs of the whole step
+    flops = 0.0
+    for b in range(B):
+        n = int(lens[b])
+        first = n - chunk + 1            # keys visible to the chunk's first row
+        flops += 4.0 * D * Hq * (chunk * first + chunk * (chunk - 1) / 2)
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < WARMUP_SECONDS:
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "chunked prefill attention TFLOP/s (causal), one layer",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": cfg.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"prefill_{cfg.name}", "batch": B, "chunk": chunk, "num_q_heads": Hq,
+                   "num_kv_heads": cfg.num_kv_heads, "head_dim": D, "page_size": cfg.page_size,
+                   "context_tokens": int(lens.sum()), "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_TFLOPS_16BIT, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS_16BIT, 4), "traffic": None},
+        "parity": parity,
+    }
+    if baseline is not None:
+        rec["cpu_baseline"] = baseline
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -607,6 +715,9 @@ def main():
         return
     if args.op == "serve":
         bench_serve(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import paged_kv_cache_266_amd as pkv
