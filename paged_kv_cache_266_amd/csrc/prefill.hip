@@ -20,8 +20,9 @@
 //    bytes per thread per chunk, gathered through the block table (tokens
 //    past the context length read as zero), and staged in LDS: K row-major
 //    (the B operand of q.k reads 8 consecutive dims of one key), V transposed
-//    (the B operand of p.V reads 8 consecutive keys of one dim).  The next
-//    tile's loads are in flight while the current tile is computed.
+//    (the B operand of p.V reads 8 consecutive keys of one dim; the lanes of
+//    a wave load one key each, so they write consecutive keys of a row).  The
+//    loads run two tiles ahead of the arithmetic (two register sets).
 //  * q.k: the wave's 16 query rows are the A operand (held in registers for
 //    the whole block), 4 dim steps of 32; scores land as row 4a + v, key
 //    16tb + c.  Keys after a row's position are masked.
@@ -173,42 +174,50 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
     const int last_pos = bad_len ? -1 : n - nq + tok_hi - 1;
     const int n_tiles = last_pos < 0 ? 0 : last_pos / kKeyTile + 1;
 
-    // ---- key-tile loads: thread tid moves chunks tid + 256 j (j < 4) of K and
-    // of V; chunk q is dims 8 (q % 16) .. +8 of key q / 16 of the tile
+    // ---- key-tile loads, two tiles in flight (register sets 0 and 1).  K:
+    // thread tid moves chunks tid + 256 j (j < 4), chunk q being dims
+    // 8 (q % 16) .. +8 of key q / 16 (rows of consecutive 16-byte pieces).  V:
+    // thread tid moves dims 8 (tid / 64 + 4 j) .. +8 of key tid % 64, so that
+    // the lanes of a wave write consecutive keys of one transposed row.
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
     const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
-    u32x4 kreg[4], vreg[4];
+    u32x4 kreg[2][4], vreg[2][4];
     bool bad = false;
-    auto load_tile = [&](int tile) {
+    // element offset of key `key` (dims from 0) in the pools, or -1 if it is
+    // not read (past the context / the block, or its page outside the pool)
+    auto key_offset = [&](int key) -> long long {
+        if (key >= n || key > last_pos)
+            return -1;
+        const int blk = key / PS;
+        const int page = blk < p.max_blocks ? bt[blk] : -1;
+        if ((unsigned)page >= (unsigned)p.num_pages) {
+            bad = true;
+            return -1;
+        }
+        return (long long)((size_t)page * page_stride + ((size_t)g * PS + key % PS) * kD);
+    };
+    auto load_tile = [&](int tile, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int qc = tid + 256 * j;
-            const int key = tile * kKeyTile + qc / 16;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (key < n && key <= last_pos) {
-                const int blk = key / PS;
-                const int page = blk < p.max_blocks ? bt[blk] : -1;
-                if ((unsigned)page < (unsigned)p.num_pages) {
-                    const size_t off = (size_t)page * page_stride + ((size_t)g * PS + key % PS) * kD + 8 * (qc % 16);
-                    kv = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool + off);
-                    vv = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool + off);
-                } else {
-                    bad = true;
-                }
-            }
-            kreg[j] = kv;
-            vreg[j] = vv;
+            const long long ko = key_offset(tile * kKeyTile + qc / 16);
+            kr[j] = ko < 0 ? u32x4{0u, 0u, 0u, 0u}
+                           : *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool + ko + 8 * (qc % 16));
+            const long long vo = key_offset(tile * kKeyTile + tid % 64);
+            vr[j] = vo < 0 ? u32x4{0u, 0u, 0u, 0u}
+                           : *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool + vo +
+                                                              8 * (tid / 64 + 4 * j));
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int qc = tid + 256 * j;
-            const int key = qc / 16, d0 = 8 * (qc % 16);
-            *reinterpret_cast<u32x4 *>(&s_k[key * kKStride + d0]) = kreg[j];
+            *reinterpret_cast<u32x4 *>(&s_k[(qc / 16) * kKStride + 8 * (qc % 16)]) = kr[j];
+            const int key = tid % 64, d0 = 8 * (tid / 64 + 4 * j);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s_vt[(d0 + e) * kVStride + key] = (uint16_t)(vreg[j][e / 2] >> (16 * (e % 2)));
+                s_vt[(d0 + e) * kVStride + key] = (uint16_t)(vr[j][e / 2] >> (16 * (e % 2)));
         }
     };
 
@@ -224,13 +233,15 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
     }
 
     if (n_tiles > 0)
-        load_tile(0);
-    for (int tile = 0; tile < n_tiles; ++tile) {
+        load_tile(0, kreg[0], vreg[0]);
+    if (n_tiles > 1)
+        load_tile(1, kreg[1], vreg[1]);
+    auto tile_body = [&](int tile, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
         __syncthreads();                    // the previous tile's LDS reads are done
-        store_tile();
+        store_tile(kr, vr);
         __syncthreads();
-        if (tile + 1 < n_tiles)
-            load_tile(tile + 1);            // in flight behind this tile's arithmetic
+        if (tile + 2 < n_tiles)
+            load_tile(tile + 2, kr, vr);    // two tiles ahead of the arithmetic
 
         // ---- scores: S[row 4a + v][key 16tb + c]
         f32x4 sc[4];
@@ -298,6 +309,11 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
             }
         });
         __builtin_amdgcn_wave_barrier();
+    };
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+        tile_body(tile, kreg[0], vreg[0]);
+        if (tile + 1 < n_tiles)
+            tile_body(tile + 1, kreg[1], vreg[1]);
     }
 
     // ---- finalize: O / l, written in q's type
