@@ -10,25 +10,33 @@
 // decode path's scaled-dot-product softmax (section 3.3 of the same page).
 //
 // Design.  One workgroup of four waves per (block of query tokens, KV head,
-// sequence).  Its 64 rows are (token, head of the group) pairs, token-major:
-// 64 / G query tokens of the G heads sharing the KV head, 16 rows per wave.
-// Both contractions run on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}:
-// D[16][16] += A[16][32] . B[32][16]; lane l = (a, c) = (l/16, l%16) supplies
-// A[c][8a + i] and B[8a + i][c], i < 8, and holds D[4a + v][c], v < 4):
+// sequence).  Its 128 rows are (token, head of the group) pairs, token-major:
+// 128 / G query tokens of the G heads sharing the KV head, 32 rows per wave.
+// Both contractions run on the matrix cores as 32 x 32 products
+// (v_mfma_f32_32x32x16_{bf16,f16}: D[32][32] += A[32][16] . B[16][32]; lane
+// l = (h, c) = (l/32, l%32) supplies A[c][8h + i] and B[8h + i][c], i < 8,
+// and holds D[8(j/4) + 4h + j%4][c], j < 16), written transposed so that
+// everything a lane needs for its softmax and output stays in its registers:
 //
-//  * K and V of a 64-token key tile are loaded by the whole workgroup, 16
-//    bytes per thread per chunk, gathered through the block table (tokens
-//    past the context length read as zero), and staged in LDS: K row-major
-//    (the B operand of q.k reads 8 consecutive dims of one key), V transposed
-//    (the B operand of p.V reads 8 consecutive keys of one dim; the lanes of
-//    a wave load one key each, so they write consecutive keys of a row).  The
-//    loads run two tiles ahead of the arithmetic (two register sets).
-//  * q.k: the wave's 16 query rows are the A operand (held in registers for
-//    the whole block), 4 dim steps of 32; scores land as row 4a + v, key
-//    16tb + c.  Keys after a row's position are masked.
-//  * Online softmax per row (running max and sum in the exp2 domain),
-//    probabilities rounded to q's type and passed through the wave's LDS slot
-//    into the A layout of p.V; O[row][dim] accumulates in 8 x 4 registers.
+//  * S^T = K . q^T per 32-key block: K (LDS, row-major) is the A operand,
+//    q (registers, the wave's 32 rows) the B operand.  Lane (h, c) ends with
+//    the scores of ONE query row (c) against 16 of the block's keys; the
+//    other 16 are in lane (1 - h, c).
+//  * Online softmax per row (running max in the exp2 domain, one lane
+//    exchange per tile for the max; the sum is combined at the end).
+//  * O^T += V^T . P^T per 16-key step: transposed V (LDS) is the A operand
+//    and the row's probabilities, rounded to q's type, are the B operand
+//    straight from the score registers -- the keys of a step are taken in
+//    the order the score layout holds them (4h .. 4h+3, 8 + 4h .. 8 + 4h + 3),
+//    and transposed V is stored with the middle quarters of every 16 keys
+//    swapped so that this order is one 16-byte read.  O^T[dim][row] lands in
+//    the lane of its row: no cross-lane work until the output.
+//  * K and V of a 64-key tile are loaded by the whole workgroup, 16 bytes per
+//    thread per piece, through the block table (one page per tile for
+//    64-token pages, four for 16-token pages; keys past the block's last
+//    position read as zero), two tiles ahead of the arithmetic (two register
+//    sets).  K is stored row-major; each thread holds four consecutive keys
+//    of eight dims of V and writes them transposed, 8 bytes per dim.
 //
 // Key tiles after the block's last position are not visited.  A sequence
 // whose context length is invalid (negative, above the bound, or shorter
@@ -53,39 +61,15 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kKeyTile = 64;          // keys per tile
-constexpr int kRows = 64;             // query rows per workgroup (4 waves x 16)
+constexpr int kRows = 128;            // query rows per workgroup (4 waves x 32)
 constexpr int kD = 128;               // head_dim
 constexpr int kKStride = kD + 8;      // LDS row of K (16-bit elements), padded
 constexpr int kVStride = kKeyTile + 8;  // LDS row of transposed V (16-bit elements), padded
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
-                                                                 false));
-}
-
-// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
-__device__ __forceinline__ float row_max16(float x)
-{
-    x = fmaxf(x, dpp<0x128>(x));
-    x = fmaxf(x, dpp<0x124>(x));
-    x = fmaxf(x, dpp<0x122>(x));
-    x = fmaxf(x, dpp<0x121>(x));
-    return x;
-}
-
-__device__ __forceinline__ float row_sum16(float x)
-{
-    x += dpp<0x128>(x);
-    x += dpp<0x124>(x);
-    x += dpp<0x122>(x);
-    x += dpp<0x121>(x);
-    return x;
-}
+typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 template <int QT>
 __device__ __forceinline__ u32 pack2(float a, float b)
@@ -100,22 +84,13 @@ __device__ __forceinline__ u32 pack2(float a, float b)
 }
 
 template <int QT>
-__device__ __forceinline__ uint16_t pack1(float a)
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
 {
     if constexpr (QT == BF16)
-        return __builtin_bit_cast(uint16_t, (__bf16)a);
-    else
-        return __builtin_bit_cast(uint16_t, (_Float16)a);
-}
-
-template <int QT>
-__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c)
-{
-    if constexpr (QT == BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                       0, 0, 0);
 }
 
@@ -126,16 +101,26 @@ __device__ __forceinline__ void static_for(F &&f)
         (std::make_integer_sequence<int, N>{});
 }
 
-template <int PS, int G, int QT>
-__global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
+// Column of key k (0..63 in the tile) in a row of transposed V: the middle
+// quarters of every 16 keys are swapped, so that keys 4h .. 4h+3 and
+// 8 + 4h .. 8 + 4h + 3 of a 16-key step sit at columns 8h .. 8h+7.
+__device__ __forceinline__ int vt_column(int k)
 {
-    constexpr int QPB = kRows / G;    // query tokens per block
-    __shared__ uint16_t s_k[kKeyTile * kKStride];
-    __shared__ uint16_t s_vt[kD * kVStride];
-    __shared__ float s_p[4][16][kKeyTile];
+    const int q = (k / 4) % 4;
+    const int sq = q == 1 ? 2 : q == 2 ? 1 : q;
+    return 16 * (k / 16) + 4 * sq + k % 4;
+}
+
+template <int PS, int G, int QT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_kernel(PrefillParams p)
+{
+    constexpr int QPB = kRows / G;            // query tokens per block
+    constexpr int PPT = kKeyTile / PS;        // pages per key tile
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeyTile * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[kD * kVStride];
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int a = lane / 16, c = lane % 16;
+    const int h = lane / 32, c = lane % 32;
     const int qblk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
 
@@ -150,88 +135,96 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
     const bool bad_len = n < 0 || n > p.max_context_len || nq > n;
     const int tok_hi = min(nq, i0 + QPB);   // this block's query tokens: [i0, tok_hi)
 
-    // this lane's A-operand row (for q) and its query
-    const int row_a = 16 * wave + c;
-    const int tok_a = i0 + row_a / G, head_a = g * G + row_a % G;
-    const bool valid_a = tok_a < tok_hi;
-    u32x4 qa[4];
+    // this lane's query row: column c of the wave's 32 rows
+    const int row = 32 * wave + c;
+    const int tok = i0 + row / G, head = g * G + row % G;
+    const bool valid_row = tok < tok_hi;
+    const int pos = valid_row && !bad_len ? n - nq + tok : -1;   // -1: masks every key
+    u32x4 qb[8];   // B operand of step s: q[row][16s + 8h .. +8]
     {
-        const char *qrow = (const char *)p.q + (((size_t)(qs0 + (valid_a ? tok_a : i0)) * Hq + head_a) * kD) * 2;
+        const char *qrow = (const char *)p.q + (((size_t)(qs0 + (valid_row ? tok : i0)) * Hq + head) * kD) * 2;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (32 * s + 8 * a) * 2);
-            qa[s] = valid_a ? v : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < 8; ++s) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (16 * s + 8 * h) * 2);
+            qb[s] = valid_row ? v : u32x4{0u, 0u, 0u, 0u};
         }
-    }
-    // positions of the rows this lane holds in the D layout (row 4a + v of the wave)
-    int pos_row[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 16 * wave + 4 * a + v;
-        const int tok = i0 + r / G;
-        pos_row[v] = tok < tok_hi && !bad_len ? n - nq + tok : -1;   // -1: masks every key
     }
     const int last_pos = bad_len ? -1 : n - nq + tok_hi - 1;
     const int n_tiles = last_pos < 0 ? 0 : last_pos / kKeyTile + 1;
 
-    // ---- key-tile loads, two tiles in flight (register sets 0 and 1).  K:
-    // thread tid moves chunks tid + 256 j (j < 4), chunk q being dims
-    // 8 (q % 16) .. +8 of key q / 16 (rows of consecutive 16-byte pieces).  V:
-    // thread tid moves dims 8 (tid / 64 + 4 j) .. +8 of key tid % 64, so that
-    // the lanes of a wave write consecutive keys of one transposed row.
+    // ---- key-tile loads.  K: thread tid moves dims 8 (tid % 16) .. +8 of
+    // keys tid / 16 + 16 j (j < 4).  V: thread tid moves dims 8 (tid / 16) ..
+    // +8 of the four keys 4 (tid % 16) + j.
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
     const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
-    u32x4 kreg[2][4], vreg[2][4];
+    const int kg = tid % 16, dv = tid / 16;
     bool bad = false;
-    // element offset of key `key` (dims from 0) in the pools, or -1 if it is
-    // not read (past the context / the block, or its page outside the pool)
-    auto key_offset = [&](int key) -> long long {
-        if (key >= n || key > last_pos)
-            return -1;
-        const int blk = key / PS;
-        const int page = blk < p.max_blocks ? bt[blk] : -1;
-        if ((unsigned)page >= (unsigned)p.num_pages) {
-            bad = true;
-            return -1;
-        }
-        return (long long)((size_t)page * page_stride + ((size_t)g * PS + key % PS) * kD);
-    };
     auto load_tile = [&](int tile, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+        int pg[PPT];
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int blk = tile * PPT + i;
+            pg[i] = blk < p.max_blocks ? bt[blk] : -1;
+        }
+        const int key0 = tile * kKeyTile;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int qc = tid + 256 * j;
-            const long long ko = key_offset(tile * kKeyTile + qc / 16);
-            kr[j] = ko < 0 ? u32x4{0u, 0u, 0u, 0u}
-                           : *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool + ko + 8 * (qc % 16));
-            const long long vo = key_offset(tile * kKeyTile + tid % 64);
-            vr[j] = vo < 0 ? u32x4{0u, 0u, 0u, 0u}
-                           : *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool + vo +
-                                                              8 * (tid / 64 + 4 * j));
+            const int kk = tid / 16 + 16 * j;
+            const int page = pg[PPT == 1 ? 0 : j];
+            const bool want = key0 + kk <= last_pos;
+            const bool inside = (unsigned)page < (unsigned)p.num_pages;
+            bad = bad || (want && !inside);
+            kr[j] = want && inside
+                        ? *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool + (size_t)page * page_stride +
+                                                           ((size_t)g * PS + kk % PS) * kD + 8 * kg)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+        int vpage = pg[0];
+        if constexpr (PPT > 1) {
+#pragma unroll
+            for (int i = 1; i < PPT; ++i)
+                vpage = kg / (PS / 4) == i ? pg[i] : vpage;
+        }
+        const bool vinside = (unsigned)vpage < (unsigned)p.num_pages;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = 4 * kg + j;
+            const bool want = key0 + kk <= last_pos;
+            bad = bad || (want && !vinside);
+            vr[j] = want && vinside
+                        ? *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool + (size_t)vpage * page_stride +
+                                                           ((size_t)g * PS + kk % PS) * kD + 8 * dv)
+                        : u32x4{0u, 0u, 0u, 0u};
         }
     };
+    const int vcol = vt_column(4 * kg);
     auto store_tile = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int qc = tid + 256 * j;
-            *reinterpret_cast<u32x4 *>(&s_k[(qc / 16) * kKStride + 8 * (qc % 16)]) = kr[j];
-            const int key = tid % 64, d0 = 8 * (tid / 64 + 4 * j);
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x4 *>(&s_k[(tid / 16 + 16 * j) * kKStride + 8 * kg]) = kr[j];
+        // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s_vt[(d0 + e) * kVStride + key] = (uint16_t)(vr[j][e / 2] >> (16 * (e % 2)));
+        for (int w = 0; w < 4; ++w) {
+            const u32 lo01 = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
+            const u32 lo23 = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
+            const u32 hi01 = (vr[0][w] >> 16) | (vr[1][w] & 0xFFFF0000u);
+            const u32 hi23 = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
+            *reinterpret_cast<u32x2 *>(&s_vt[(8 * dv + 2 * w) * kVStride + vcol]) = u32x2{lo01, lo23};
+            *reinterpret_cast<u32x2 *>(&s_vt[(8 * dv + 2 * w + 1) * kVStride + vcol]) = u32x2{hi01, hi23};
         }
     };
 
-    f32x4 acc[8];   // O[row 4a + v][dim 16nb + c] in acc[nb][v]
+    f32x16 oacc[4];   // O^T[dim 32 db + 8 (j/4) + 4 h + j%4][row c] in oacc[db][j]
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-        acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_row[4], l_row[4];
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        m_row[v] = -INFINITY;
-        l_row[v] = 0.0f;
-    }
+        for (int j = 0; j < 16; ++j)
+            oacc[db][j] = 0.0f;
+    // running max starts finite: a row with no visible key yet gets alpha 1
+    // and probabilities 0, never (-inf) - (-inf)
+    float m_run = -3.0e38f, l_run = 0.0f;
 
+    u32x4 kreg[2][4], vreg[2][4];
     if (n_tiles > 0)
         load_tile(0, kreg[0], vreg[0]);
     if (n_tiles > 1)
@@ -243,72 +236,72 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
         if (tile + 2 < n_tiles)
             load_tile(tile + 2, kr, vr);    // two tiles ahead of the arithmetic
 
-        // ---- scores: S[row 4a + v][key 16tb + c]
-        f32x4 sc[4];
-        static_for<4>([&](auto TBc) {
-            constexpr int TB = decltype(TBc)::value;
-            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+        // ---- scores S^T[key 32 kb + 8 (j/4) + 4 h + j%4][row c] in sc[kb][j]
+        f32x16 sc[2];
+        static_for<2>([&](auto KBc) {
+            constexpr int KB = decltype(KBc)::value;
+            f32x16 x;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4 kop = *reinterpret_cast<const u32x4 *>(&s_k[(16 * TB + c) * kKStride + 32 * s + 8 * a]);
-                x = mfma32<QT>(qa[s], kop, x);
+            for (int j = 0; j < 16; ++j)
+                x[j] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 kop = *reinterpret_cast<const u32x4 *>(&s_k[(32 * KB + c) * kKStride + 16 * s + 8 * h]);
+                x = mfma32<QT>(kop, qb[s], x);
             }
-            sc[TB] = x;
+            sc[KB] = x;
         });
 
-        // ---- online softmax (log2 domain) with the causal mask
-        const int key0 = tile * kKeyTile;
+        // ---- online softmax of row c (log2 domain) with the causal mask
+        const int key0 = tile * kKeyTile + 4 * h;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float mx = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const float x = key0 + 16 * tb + c <= pos_row[v] ? sc[tb][v] * p.scale_log2 : -INFINITY;
-                sc[tb][v] = x;
+            for (int j = 0; j < 16; ++j) {
+                const int key = key0 + 32 * kb + 8 * (j / 4) + j % 4;
+                const float x = key <= pos ? sc[kb][j] * p.scale_log2 : -INFINITY;
+                sc[kb][j] = x;
                 mx = fmaxf(mx, x);
             }
-            const float m_new = fmaxf(m_row[v], row_max16(mx));
-            // a row with no key yet keeps m = -inf; exp2 of (-inf) - (-inf) is avoided
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_row[v] - m_new);
-            float ls = 0.0f;
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ls = 0.0f;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const float e = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[tb][v] - m_new);
-                sc[tb][v] = e;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float e = __builtin_amdgcn_exp2f(sc[kb][j] - m_new);
+                sc[kb][j] = e;
                 ls += e;
             }
-            l_row[v] = l_row[v] * alpha + ls;
-            m_row[v] = m_new;
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-                acc[nb][v] *= alpha;
-        }
-        // probabilities to the wave's LDS slot, [row][key]
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                s_p[wave][4 * a + v][16 * tb + c] = sc[tb][v];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int j = 0; j < 16; ++j)
+                oacc[db][j] *= alpha;
 
-        // ---- p.V: A[row c][key 32ks + 8a + i] from LDS, B[key][dim 16nb + c] from transposed V
-        static_for<2>([&](auto KSc) {
-            constexpr int KS = decltype(KSc)::value;
-            const float *src = &s_p[wave][c][32 * KS + 8 * a];
-            const float4 p0 = *reinterpret_cast<const float4 *>(src);
-            const float4 p1 = *reinterpret_cast<const float4 *>(src + 4);
-            const u32x4 aop = {pack2<QT>(p0.x, p0.y), pack2<QT>(p0.z, p0.w), pack2<QT>(p1.x, p1.y),
-                               pack2<QT>(p1.z, p1.w)};
+        // ---- P^T operand of 16-key step ks: keys 16 ks + 4h .. +3, 16 ks + 8 + 4h .. +3
+        u32x4 pb[4];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kb = ks / 2, j0 = 8 * (ks % 2);
+            pb[ks] = u32x4{pack2<QT>(sc[kb][j0], sc[kb][j0 + 1]), pack2<QT>(sc[kb][j0 + 2], sc[kb][j0 + 3]),
+                           pack2<QT>(sc[kb][j0 + 4], sc[kb][j0 + 5]), pack2<QT>(sc[kb][j0 + 6], sc[kb][j0 + 7])};
+        }
+        // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row]
+        static_for<4>([&](auto DBc) {
+            constexpr int DB = decltype(DBc)::value;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 vop =
-                    *reinterpret_cast<const u32x4 *>(&s_vt[(16 * nb + c) * kVStride + 32 * KS + 8 * a]);
-                acc[nb] = mfma32<QT>(aop, vop, acc[nb]);
+                    *reinterpret_cast<const u32x4 *>(&s_vt[(32 * DB + c) * kVStride + 16 * ks + 8 * h]);
+                oacc[DB] = mfma32<QT>(vop, pb[ks], oacc[DB]);
             }
         });
-        __builtin_amdgcn_wave_barrier();
     };
     for (int tile = 0; tile < n_tiles; tile += 2) {
         tile_body(tile, kreg[0], vreg[0]);
@@ -318,21 +311,20 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams p)
 
     // ---- finalize: O / l, written in q's type
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_len;
-    const float nan = __builtin_nanf("");
+    const float l = l_run + __shfl_xor(l_run, 32);
+    if (!valid_row)
+        return;
+    const float inv = any_bad ? __builtin_nanf("") : 1.0f / l;
+    u32x2 *orow = reinterpret_cast<u32x2 *>((uint16_t *)p.out + ((size_t)(qs0 + tok) * Hq + head) * kD);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 16 * wave + 4 * a + v;
-        const int tok = i0 + r / G;
-        if (tok >= tok_hi)
-            continue;
-        const int head = g * G + r % G;
-        const float l = row_sum16(l_row[v]);
-        const float inv = any_bad ? nan : 1.0f / l;
-        uint16_t *orow = (uint16_t *)p.out + ((size_t)(qs0 + tok) * Hq + head) * kD;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-            orow[16 * nb + c] = pack1<QT>(acc[nb][v] * inv);
-    }
+        for (int j4 = 0; j4 < 4; ++j4) {
+            // dims 32 db + 8 j4 + 4 h .. +3
+            const int j = 4 * j4;
+            orow[(32 * db + 8 * j4 + 4 * h) / 4] = u32x2{pack2<QT>(oacc[db][j] * inv, oacc[db][j + 1] * inv),
+                                                        pack2<QT>(oacc[db][j + 2] * inv, oacc[db][j + 3] * inv)};
+        }
 }
 
 template <int PS, int G>
