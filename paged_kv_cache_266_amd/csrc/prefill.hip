@@ -35,8 +35,9 @@
 //    thread per piece, through the block table (one page per tile for
 //    64-token pages, four for 16-token pages; keys past the block's last
 //    position read as zero), two tiles ahead of the arithmetic (two register
-//    sets).  K is stored row-major; each thread holds four consecutive keys
-//    of eight dims of V and writes them transposed, 8 bytes per dim.
+//    sets), and stored to LDS one tile ahead (two LDS buffers, one barrier
+//    per tile).  K is stored row-major; each thread holds four consecutive
+//    keys of eight dims of V and writes them transposed, 8 bytes per dim.
 //
 // Key tiles after the block's last position are not visited.  A sequence
 // whose context length is invalid (negative, above the bound, or shorter
@@ -116,8 +117,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 {
     constexpr int QPB = kRows / G;            // query tokens per block
     constexpr int PPT = kKeyTile / PS;        // pages per key tile
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeyTile * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[kD * kVStride];
+    // two buffers: tile t is read from buffer t % 2 while tile t + 1 is stored
+    // into the other one
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeyTile * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVStride];
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int h = lane / 32, c = lane % 32;
@@ -140,12 +143,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int tok = i0 + row / G, head = g * G + row % G;
     const bool valid_row = tok < tok_hi;
     const int pos = valid_row && !bad_len ? n - nq + tok : -1;   // -1: masks every key
+    // A negative scale is applied as |scale| to -q (a sign flip, exact), so
+    // that the row maximum of the raw scores is the maximum of the scaled
+    // ones.  A zero scale is taken as 1e-30: 2^(1e-30 s) rounds to exactly 1
+    // for any finite score s below 1e22, and a masked key (-inf) still gives 0.
+    const float scale = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
+    const u32 qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
     u32x4 qb[8];   // B operand of step s: q[row][16s + 8h .. +8]
     {
         const char *qrow = (const char *)p.q + (((size_t)(qs0 + (valid_row ? tok : i0)) * Hq + head) * kD) * 2;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (16 * s + 8 * h) * 2);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (16 * s + 8 * h) * 2) ^ qsign;
             qb[s] = valid_row ? v : u32x4{0u, 0u, 0u, 0u};
         }
     }
@@ -198,10 +207,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
     const int vcol = vt_column(4 * kg);
-    auto store_tile = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
+    auto store_tile = [&](int buf, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4 *>(&s_k[(tid / 16 + 16 * j) * kKStride + 8 * kg]) = kr[j];
+            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / 16 + 16 * j) * kKStride + 8 * kg]) = kr[j];
         // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -209,8 +218,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const u32 lo23 = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
             const u32 hi01 = (vr[0][w] >> 16) | (vr[1][w] & 0xFFFF0000u);
             const u32 hi23 = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
-            *reinterpret_cast<u32x2 *>(&s_vt[(8 * dv + 2 * w) * kVStride + vcol]) = u32x2{lo01, lo23};
-            *reinterpret_cast<u32x2 *>(&s_vt[(8 * dv + 2 * w + 1) * kVStride + vcol]) = u32x2{hi01, hi23};
+            *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w) * kVStride + vcol]) = u32x2{lo01, lo23};
+            *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w + 1) * kVStride + vcol]) = u32x2{hi01, hi23};
         }
     };
 
@@ -220,21 +229,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             oacc[db][j] = 0.0f;
-    // running max starts finite: a row with no visible key yet gets alpha 1
-    // and probabilities 0, never (-inf) - (-inf)
+    // Reference max of the row's exponentials, in log2 units.  It starts
+    // finite (a row with no visible key yet gets probabilities 0, never
+    // (-inf) - (-inf)) and is raised only when a tile's max exceeds it by more
+    // than kSlack: the probabilities then stay below 2^kSlack, and O and the
+    // sum, scaled by the same stale reference, still give O / sum exactly.
+    constexpr float kSlack = 8.0f;
     float m_run = -3.0e38f, l_run = 0.0f;
 
+    // Register set k % 2 carries tile k from its load to its LDS store; the
+    // loads run two tiles ahead of the arithmetic, the stores one.
     u32x4 kreg[2][4], vreg[2][4];
     if (n_tiles > 0)
         load_tile(0, kreg[0], vreg[0]);
     if (n_tiles > 1)
         load_tile(1, kreg[1], vreg[1]);
-    auto tile_body = [&](int tile, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-        __syncthreads();                    // the previous tile's LDS reads are done
-        store_tile(kr, vr);
+    if (n_tiles > 0) {
+        store_tile(0, kreg[0], vreg[0]);
+        if (n_tiles > 2)
+            load_tile(2, kreg[0], vreg[0]);
+    }
+    // tile `tile` is in LDS buffer BUF; kr / vr hold tile + 1
+    auto tile_body = [&](int tile, auto BUFc, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+        constexpr int BUF = decltype(BUFc)::value;
+        // every wave is done with tile - 1 (buffer 1 - BUF), and tile's
+        // stores (buffer BUF) are complete
         __syncthreads();
-        if (tile + 2 < n_tiles)
-            load_tile(tile + 2, kr, vr);    // two tiles ahead of the arithmetic
+        if (tile + 1 < n_tiles) {
+            store_tile(1 - BUF, kr, vr);
+            if (tile + 3 < n_tiles)
+                load_tile(tile + 3, kr, vr);
+        }
 
         // ---- scores S^T[key 32 kb + 8 (j/4) + 4 h + j%4][row c] in sc[kb][j]
         f32x16 sc[2];
@@ -246,43 +271,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 x[j] = 0.0f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const u32x4 kop = *reinterpret_cast<const u32x4 *>(&s_k[(32 * KB + c) * kKStride + 16 * s + 8 * h]);
+                const u32x4 kop =
+                    *reinterpret_cast<const u32x4 *>(&s_k[BUF][(32 * KB + c) * kKStride + 16 * s + 8 * h]);
                 x = mfma32<QT>(kop, qb[s], x);
             }
             sc[KB] = x;
         });
 
-        // ---- online softmax of row c (log2 domain) with the causal mask
+        // ---- online softmax of row c (log2 domain).  The causal mask is
+        // needed only in tiles that reach past some valid row's position.
         const int key0 = tile * kKeyTile + 4 * h;
+        const bool masked = __builtin_amdgcn_ballot_w64(valid_row && tile * kKeyTile + kKeyTile - 1 > pos) != 0;
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = key0 + 32 * kb + 8 * (j / 4) + j % 4;
+                    sc[kb][j] = key <= pos ? sc[kb][j] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = key0 + 32 * kb + 8 * (j / 4) + j % 4;
-                const float x = key <= pos ? sc[kb][j] * p.scale_log2 : -INFINITY;
-                sc[kb][j] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            for (int j = 0; j < 16; ++j)
+                mx = fmaxf(mx, sc[kb][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale;
+        const bool grow = mx > m_run + kSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    oacc[db][j] *= alpha;
+        }
         float ls = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float e = __builtin_amdgcn_exp2f(sc[kb][j] - m_new);
+                // a masked key (-inf) gives 0
+                const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][j], scale, -m_run));
                 sc[kb][j] = e;
                 ls += e;
             }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                oacc[db][j] *= alpha;
+        l_run += ls;
 
         // ---- P^T operand of 16-key step ks: keys 16 ks + 4h .. +3, 16 ks + 8 + 4h .. +3
         u32x4 pb[4];
@@ -298,15 +336,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 vop =
-                    *reinterpret_cast<const u32x4 *>(&s_vt[(32 * DB + c) * kVStride + 16 * ks + 8 * h]);
+                    *reinterpret_cast<const u32x4 *>(&s_vt[BUF][(32 * DB + c) * kVStride + 16 * ks + 8 * h]);
                 oacc[DB] = mfma32<QT>(vop, pb[ks], oacc[DB]);
             }
         });
     };
     for (int tile = 0; tile < n_tiles; tile += 2) {
-        tile_body(tile, kreg[0], vreg[0]);
+        tile_body(tile, std::integral_constant<int, 0>{}, kreg[1], vreg[1]);
         if (tile + 1 < n_tiles)
-            tile_body(tile + 1, kreg[1], vreg[1]);
+            tile_body(tile + 1, std::integral_constant<int, 1>{}, kreg[0], vreg[0]);
     }
 
     // ---- finalize: O / l, written in q's type

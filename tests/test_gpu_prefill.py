@@ -74,7 +74,7 @@ CHUNKS = (1, 63, 20, 65, 100, 130)
 @pytest.mark.parametrize("PS,G,qd", list(itertools.product((16, 64), (1, 2, 4, 8), ("f16", "bf16"))))
 def test_prefill_every_instantiation(PS, G, qd):
     """Ragged chunks: a whole 1-token sequence, a whole 63-token one, parts
-    of longer ones, chunks spanning several query blocks (64/G tokens each)
+    of longer ones, chunks spanning several query blocks (128/G tokens each)
     and key tiles."""
     Hkv = 2
     cfg = small_config(G * Hkv, Hkv, 128, qd, qd, PS, LENS)
@@ -84,6 +84,21 @@ def test_prefill_every_instantiation(PS, G, qd):
     got = gpu_prefill(case, qb, qs)
     ref = oracle.paged_prefill(case, qb, qs)
     check(case, got, ref, "all rows")
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 1.0, 4.0])
+def test_prefill_scales(scale):
+    """A negative scale, a zero scale (uniform weights over the visible keys),
+    and scales large enough that rows' running maxima rise by many powers of
+    two after the first key tile, so the kernel's deferred rescaling runs
+    mid-sequence."""
+    cfg = small_config(8, 2, 128, "f16", "f16", 64, (300, 777, 1000))
+    case = dataclasses.replace(make_case(cfg, seed=21), scale=scale)
+    qb, qs = queries(cfg, (100, 200, 130), seed=22)
+    note(f"[prefill scale] {scale}")
+    got = gpu_prefill(case, qb, qs)
+    ref = oracle.paged_prefill(case, qb, qs)
+    check(case, got, ref, f"scale {scale}")
 
 
 def test_prefill_empty_chunks_and_invalid_lengths():
