@@ -795,18 +795,25 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    # the timed region: K whole steps (one library call each), nothing else
+    # the timed region: K whole steps (one library call, one kernel launch
+    # each), nothing else, bracketed by HIP events on the launch stream; their
+    # span / K is the kernel's average duration for the roofline
+    region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = wall_ms / args.steps
     value = bytes_alg / (ms_per_step * 1e-3) / 1e9
+    launch_ms = region[0].elapsed_time(region[1]) / args.steps
 
-    # a second pass of K steps with HIP events on the launch stream around
-    # each call (one kernel launch): the kernel's duration for the roofline
+    # a second pass of K steps with an event pair around each launch: the
+    # spread of launch durations (each pair adds its own overhead, so these
+    # read a little above the timed region's average)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -814,7 +821,7 @@ def main():
     torch.cuda.synchronize()
     kern_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
 
-    achieved = bytes_alg / (kern_ms.mean() * 1e-3) / 1e9
+    achieved = bytes_alg / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(cfg.name)
     result = {
         "metric": "paged-attn decode HBM GB/s (% of 8 TB/s peak), us per layer-step",
@@ -839,6 +846,7 @@ def main():
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "kernel_us_timed_region": round(launch_ms * 1e3, 2),
         "kernel_event_us": {
             "mean": round(float(kern_ms.mean()) * 1e3, 2),
             "median": round(float(np.median(kern_ms)) * 1e3, 2),
