@@ -398,7 +398,8 @@ typedef struct pkv_prefill_args {
  * than its chunk gets NaN rows, as does any block of rows that needs a page
  * outside the pool; rows of a sequence whose q_start entries are out of
  * order or beyond n_q are not written.  UNSUPPORTED outside the instantiated
- * shapes; INVALID_ARG for bad sizes or null pointers. */
+ * shapes; INVALID_ARG for bad sizes (batch and num_kv_heads at most 65535
+ * each) or null pointers. */
 pkv_status pkv_paged_prefill(const pkv_prefill_args *args, void *stream);
 
 /* ===================================================================== *

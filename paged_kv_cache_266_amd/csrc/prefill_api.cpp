@@ -40,8 +40,9 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: null device pointer");
     if ((uintptr_t)a->q % 16 || (uintptr_t)a->k_pool % 16 || (uintptr_t)a->v_pool % 16)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: q and pools must be 16-byte aligned");
-    if ((int64_t)a->batch * a->num_kv_heads > 65535 || (int64_t)a->batch > 65535)
-        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: batch too large for one launch");
+    // one launch: grid (query blocks, KV heads, sequences)
+    if (a->batch > 65535 || a->num_kv_heads > 65535)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: batch and num_kv_heads must be at most 65535");
     pkv::PrefillParams p{};
     p.q = a->q;
     p.k_pool = a->k_pool;
