@@ -165,16 +165,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // keys tid / 16 + 16 j (j < 4).  V: thread tid moves dims 8 (tid / 16) ..
     // +8 of the four keys 4 (tid % 16) + j.
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
-    const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks;
+    // The block table is only read here: through the constant address space
+    // its (wave-uniform) entries are scalar loads, which are counted apart
+    // from the K/V loads in flight.
+    typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+    const const_i32p bt = (const_i32p)(uintptr_t)(p.block_tables + (size_t)b * p.max_blocks);
     const int kg = tid % 16, dv = tid / 16;
     bool bad = false;
-    auto load_tile = [&](int tile, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-        int pg[PPT];
+    // Physical pages of a tile, one per 16 or 64 keys, -1 for none.  They are
+    // read one iteration before the tile's loads are issued, so that the wait
+    // for them never drains the loads in flight.
+    auto fetch_pages = [&](int tile, int (&pg)[PPT]) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int blk = tile * PPT + i;
-            pg[i] = blk < p.max_blocks ? bt[blk] : -1;
+            pg[i] = bt[min(blk, p.max_blocks - 1)];
+            pg[i] = blk < p.max_blocks ? pg[i] : -1;
         }
+    };
+    // Every load is issued, from page 0 when the key's page is outside the
+    // pool, with no branch around it and no use of its value until the LDS
+    // store, so the compiler can keep two tiles in flight.  K of keys past the
+    // block's last position needs no clearing: their scores are masked (the
+    // tile then reaches past every valid row's position) and the mask replaces
+    // the value.  V of those keys is cleared at the store (vm: one bit per
+    // key this thread holds), since a zero probability times a NaN would
+    // still be NaN.
+    auto load_tile = [&](int tile, const int (&pg)[PPT], u32x4 (&kr)[4], u32x4 (&vr)[4], unsigned &vm) {
         const int key0 = tile * kKeyTile;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -183,10 +200,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const bool want = key0 + kk <= last_pos;
             const bool inside = (unsigned)page < (unsigned)p.num_pages;
             bad = bad || (want && !inside);
-            kr[j] = want && inside
-                        ? *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool + (size_t)page * page_stride +
-                                                           ((size_t)g * PS + kk % PS) * kD + 8 * kg)
-                        : u32x4{0u, 0u, 0u, 0u};
+            kr[j] = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool +
+                                                     (size_t)(inside ? page : 0) * page_stride +
+                                                     ((size_t)g * PS + kk % PS) * kD + 8 * kg);
         }
         int vpage = pg[0];
         if constexpr (PPT > 1) {
@@ -195,19 +211,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 vpage = kg / (PS / 4) == i ? pg[i] : vpage;
         }
         const bool vinside = (unsigned)vpage < (unsigned)p.num_pages;
+        vm = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kk = 4 * kg + j;
             const bool want = key0 + kk <= last_pos;
             bad = bad || (want && !vinside);
-            vr[j] = want && vinside
-                        ? *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool + (size_t)vpage * page_stride +
-                                                           ((size_t)g * PS + kk % PS) * kD + 8 * dv)
-                        : u32x4{0u, 0u, 0u, 0u};
+            vm |= want && vinside ? 1u << j : 0u;
+            vr[j] = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool +
+                                                     (size_t)(vinside ? vpage : 0) * page_stride +
+                                                     ((size_t)g * PS + kk % PS) * kD + 8 * dv);
         }
     };
     const int vcol = vt_column(4 * kg);
-    auto store_tile = [&](int buf, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
+    auto store_tile = [&](int buf, const u32x4 (&kr)[4], const u32x4 (&vraw)[4], unsigned vm) {
+        u32x4 vr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            vr[j] = (vm >> j) & 1u ? vraw[j] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / 16 + 16 * j) * kKStride + 8 * kg]) = kr[j];
@@ -237,28 +258,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     constexpr float kSlack = 8.0f;
     float m_run = -3.0e38f, l_run = 0.0f;
 
-    // Register set k % 2 carries tile k from its load to its LDS store; the
-    // loads run two tiles ahead of the arithmetic, the stores one.
-    u32x4 kreg[2][4], vreg[2][4];
-    if (n_tiles > 0)
-        load_tile(0, kreg[0], vreg[0]);
-    if (n_tiles > 1)
-        load_tile(1, kreg[1], vreg[1]);
+    // One register set carries tile t + 1 from its loads (issued while tile
+    // t - 1 is computed) to its LDS store (before tile t is computed); the
+    // pages of a tile are read one iteration before its loads.  Loads are
+    // issued for every tile index, clamped to the last tile (whose extra copies
+    // are never read), so that no branch surrounds a load or a store and the
+    // waits before the stores cover exactly the loads they need.
+    u32x4 kreg[4], vreg[4];
+    unsigned vmask = 0;
+    int pgn[PPT];   // pages of the next tile to load
+    const int last_tile = n_tiles - 1;
     if (n_tiles > 0) {
-        store_tile(0, kreg[0], vreg[0]);
-        if (n_tiles > 2)
-            load_tile(2, kreg[0], vreg[0]);
+        fetch_pages(0, pgn);
+        load_tile(0, pgn, kreg, vreg, vmask);
+        store_tile(0, kreg, vreg, vmask);
+        fetch_pages(min(1, last_tile), pgn);
+        load_tile(min(1, last_tile), pgn, kreg, vreg, vmask);
+        fetch_pages(min(2, last_tile), pgn);
     }
-    // tile `tile` is in LDS buffer BUF; kr / vr hold tile + 1
-    auto tile_body = [&](int tile, auto BUFc, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    // tile `tile` is in LDS buffer BUF; kreg / vreg hold tile + 1
+    auto tile_body = [&](int tile, auto BUFc) {
         constexpr int BUF = decltype(BUFc)::value;
         // every wave is done with tile - 1 (buffer 1 - BUF), and tile's
         // stores (buffer BUF) are complete
         __syncthreads();
-        if (tile + 1 < n_tiles) {
-            store_tile(1 - BUF, kr, vr);
-            if (tile + 3 < n_tiles)
-                load_tile(tile + 3, kr, vr);
+        store_tile(1 - BUF, kreg, vreg, vmask);   // unread when tile + 1 is the pad tile or past it
+        {
+            int pg[PPT];
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                pg[i] = pgn[i];
+            fetch_pages(min(tile + 3, last_tile), pgn);   // before this tile's loads
+            load_tile(min(tile + 2, last_tile), pg, kreg, vreg, vmask);
         }
 
         // ---- scores S^T[key 32 kb + 8 (j/4) + 4 h + j%4][row c] in sc[kb][j]
@@ -341,10 +372,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
         });
     };
+    // An odd tile count gets one pad tile: its keys lie past every row's
+    // position, so its probabilities (and its cleared V) are zero.  Both
+    // halves of the unrolled loop then always run, with no branch around a
+    // load or store, which keeps the waits before the stores partial.
     for (int tile = 0; tile < n_tiles; tile += 2) {
-        tile_body(tile, std::integral_constant<int, 0>{}, kreg[1], vreg[1]);
-        if (tile + 1 < n_tiles)
-            tile_body(tile + 1, std::integral_constant<int, 1>{}, kreg[0], vreg[0]);
+        tile_body(tile, std::integral_constant<int, 0>{});
+        tile_body(tile + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- finalize: O / l, written in q's type
