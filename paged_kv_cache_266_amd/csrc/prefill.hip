@@ -22,8 +22,11 @@
 //    q (registers, the wave's 32 rows) the B operand.  Lane (h, c) ends with
 //    the scores of ONE query row (c) against 16 of the block's keys; the
 //    other 16 are in lane (1 - h, c).
-//  * Online softmax per row (running max in the exp2 domain, one lane
-//    exchange per tile for the max; the sum is combined at the end).
+//  * Online softmax per row in the exp2 domain: one lane exchange per tile
+//    for the max, the sum combined at the end.  The causal mask is applied
+//    only on tiles that reach past a valid row's position, and the
+//    reference max is raised only when a tile's max passes it by more than
+//    2^8, so O is rarely rescaled.
 //  * O^T += V^T . P^T per 16-key step: transposed V (LDS) is the A operand
 //    and the row's probabilities, rounded to q's type, are the B operand
 //    straight from the score registers -- the keys of a step are taken in
@@ -33,11 +36,14 @@
 //    the lane of its row: no cross-lane work until the output.
 //  * K and V of a 64-key tile are loaded by the whole workgroup, 16 bytes per
 //    thread per piece, through the block table (one page per tile for
-//    64-token pages, four for 16-token pages; keys past the block's last
-//    position read as zero), two tiles ahead of the arithmetic (two register
-//    sets), and stored to LDS one tile ahead (two LDS buffers, one barrier
-//    per tile).  K is stored row-major; each thread holds four consecutive
-//    keys of eight dims of V and writes them transposed, 8 bytes per dim.
+//    64-token pages, four for 16-token pages, read as scalar loads a tile
+//    early).  The loads are issued one tile before their LDS store (one
+//    register set) and the stores one tile before the arithmetic (two LDS
+//    buffers, one barrier per tile), with no branch around a load or a
+//    store, so the waits before the stores cover only the loads they need.
+//    V of keys past the block's last position is cleared at the store.  K is
+//    stored row-major; each thread holds four consecutive keys of eight dims
+//    of V and writes them transposed, 8 bytes per dim.
 //
 // Key tiles after the block's last position are not visited.  A sequence
 // whose context length is invalid (negative, above the bound, or shorter
