@@ -580,7 +580,7 @@ PEAK_MFMA_TFLOPS_16BIT = 2500.0   # MI355X dense bf16 / f16
 def bench_prefill(args) -> None:
     """One chunked-prefill step: every sequence of the workload processes a
     chunk of 512 new tokens at the end of its context (lengths from the
-    workload's law, at least 512), 16-bit K/V.  FLOPs counted causally:
+    workload's law, at least 512), the workload's K/V type.  FLOPs counted causally:
     4 * head_dim per (query row, query head, visible key).  The cpu_baseline
     leg runs the fp64 oracle on the last 64 rows of every chunk (about 10 s
     on 16 host cores), which is also the parity check of those rows."""
@@ -597,8 +597,8 @@ def bench_prefill(args) -> None:
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     base = CONFIGS[args.config]
-    if base.kv_dtype not in ("f16", "bf16") or base.head_dim != 128:
-        raise SystemExit("prefill: 16-bit K/V at head_dim 128 only")
+    if base.head_dim != 128:
+        raise SystemExit("prefill: head_dim 128 only")
     chunk = 512
     rng = np.random.default_rng(base.seed)
     lens = np.maximum(draw_context_lens(base, rng), chunk).astype(np.int32)
@@ -615,12 +615,13 @@ def bench_prefill(args) -> None:
 
     def step():
         pkv.paged_prefill(q, dev.k_pool, dev.v_pool, dev.block_tables, qs, dev.context_lens, case.scale,
-                          max_context_len=cfg.max_context_len, max_q_len=chunk, out=out)
+                          max_context_len=cfg.max_context_len, max_q_len=chunk, out=out,
+                          k_scale=dev.k_scale, v_scale=dev.v_scale)
 
     step()
     torch.cuda.synchronize()
     got = out.to(torch.float64).cpu().numpy()
-    tol = {"f16": 4e-3, "bf16": 1.6e-2}[cfg.kv_dtype]
+    tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}[cfg.kv_dtype]
     parity, baseline = {"ok": None, "note": "not checked: --no-cpu-baseline"}, None
     if not args.no_cpu_baseline:
         import dataclasses
@@ -669,6 +670,7 @@ def bench_prefill(args) -> None:
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": cfg.kv_dtype,
         "data": "synthetic",
         "config": {"workload": f"prefill_{cfg.name}", "batch": B, "chunk": chunk, "num_q_heads": Hq,
+                   "q_dtype": cfg.q_dtype, "kv_dtype": cfg.kv_dtype,
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": D, "page_size": cfg.page_size,
                    "context_tokens": int(lens.sum()), "flops_per_step": flops},
         "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel", "achieved": round(achieved, 2),

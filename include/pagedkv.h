@@ -365,8 +365,8 @@ typedef struct pkv_prefill_args {
     const void *q;              /* device [n_q][num_q_heads][head_dim], q_dtype: the
                                    new tokens' queries, sequence after sequence       */
     const void *k_pool;         /* device pools [num_pages][num_kv_heads][page_size]
-                                   [head_dim], kv_dtype (== q_dtype); the chunk's own
-                                   K/V already written (pkv_write_kv)                 */
+                                   [head_dim], kv_dtype; the chunk's own K/V already
+                                   written (pkv_write_kv)                             */
     const void *v_pool;
     const int32_t *block_tables; /* device [batch][max_blocks], as for decode         */
     const int32_t *q_start;     /* device [batch + 1]: sequence b's queries are rows
@@ -389,8 +389,12 @@ typedef struct pkv_prefill_args {
                                    page_size)                                         */
     int32_t max_q_len;          /* host bound on every sequence's chunk length       */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16                               */
-    pkv_dtype kv_dtype;         /* == q_dtype                                        */
+    pkv_dtype kv_dtype;         /* == q_dtype, or PKV_I8 / PKV_FP8_E4M3 (then the
+                                   value of a code is code x its token's scale)      */
     float scale;
+    const float *k_scale;       /* device [num_pages][num_kv_heads][page_size] fp32,
+                                   4-byte aligned: int8 / fp8 K/V only, else NULL    */
+    const float *v_scale;
 } pkv_prefill_args;
 
 /* Chunked prefill attention; one launch, asynchronous on `stream`.  A

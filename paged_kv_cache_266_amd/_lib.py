@@ -96,6 +96,7 @@ class PrefillArgs(ctypes.Structure):
         ("num_pages", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
         ("max_q_len", ctypes.c_int32), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
         ("scale", ctypes.c_float),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 

@@ -104,6 +104,8 @@ struct PrefillParams {
     const void *q;
     const void *k_pool;
     const void *v_pool;
+    const float *k_scale;   // int8 / fp8 K/V: [num_pages][Hkv][page_size]
+    const float *v_scale;
     const int32_t *block_tables;
     const int32_t *q_start;
     const int32_t *context_lens;
@@ -117,6 +119,7 @@ struct PrefillParams {
     int32_t max_context_len;
     int32_t max_q_len;
     int32_t q_dtype;
+    int32_t kv_dtype;
     float scale_log2;     // softmax scale * log2(e)
 };
 

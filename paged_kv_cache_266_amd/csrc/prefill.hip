@@ -108,6 +108,34 @@ __device__ __forceinline__ void static_for(F &&f)
         (std::make_integer_sequence<int, N>{});
 }
 
+// Eight int8 or OCP E4M3 codes (w.x bytes 0..3, w.y bytes 0..3) widened to
+// eight values of q's 16-bit type, exactly (every int8 and every E4M3 value
+// is a bf16 and an f16 value); 16-bit K/V pass through.
+template <int QT, int KVT, class Raw>
+__device__ __forceinline__ u32x4 widen(const Raw &w)
+{
+    if constexpr (KVT == FP8) {
+        auto pair = [](u32 x, auto HIc) -> u32 {
+            constexpr bool HI = decltype(HIc)::value;
+            if constexpr (QT == BF16)
+                return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+            else
+                return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+        };
+        const std::false_type lo{};
+        const std::true_type hi{};
+        return u32x4{pair(w.x, lo), pair(w.x, hi), pair(w.y, lo), pair(w.y, hi)};
+    } else if constexpr (KVT == I8) {
+        auto pair = [](u32 x, int sh) -> u32 {
+            const float a = (float)(int8_t)(x >> sh), b = (float)(int8_t)(x >> (sh + 8));
+            return pack2<QT>(a, b);
+        };
+        return u32x4{pair(w.x, 0), pair(w.x, 16), pair(w.y, 0), pair(w.y, 16)};
+    } else {
+        return w;
+    }
+}
+
 // Column of key k (0..63 in the tile) in a row of transposed V: the middle
 // quarters of every 16 keys are swapped, so that keys 4h .. 4h+3 and
 // 8 + 4h .. 8 + 4h + 3 of a 16-key step sit at columns 8h .. 8h+7.
@@ -118,15 +146,22 @@ __device__ __forceinline__ int vt_column(int k)
     return 16 * (k / 16) + 4 * sq + k % 4;
 }
 
-template <int PS, int G, int QT>
+template <int PS, int G, int QT, int KVT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_kernel(PrefillParams p)
 {
     constexpr int QPB = kRows / G;            // query tokens per block
     constexpr int PPT = kKeyTile / PS;        // pages per key tile
+    // byte K/V (int8 or E4M3 codes with one fp32 scale per token and KV head):
+    // 8-byte pieces, widened to q's type at the LDS store
+    constexpr bool kByte = KVT == I8 || KVT == FP8;
+    constexpr int EB = kByte ? 1 : 2;         // bytes per K/V element
+    using Raw = std::conditional_t<kByte, u32x2, u32x4>;
     // two buffers: tile t is read from buffer t % 2 while tile t + 1 is stored
     // into the other one
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeyTile * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVStride];
+    // byte K/V: the tile's K scales (row 0) and V scales (row 1), per key
+    __shared__ __attribute__((aligned(16))) float s_sc[2][2][kByte ? kKeyTile : 4];
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int h = lane / 32, c = lane % 32;
@@ -197,7 +232,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // the value.  V of those keys is cleared at the store (vm: one bit per
     // key this thread holds), since a zero probability times a NaN would
     // still be NaN.
-    auto load_tile = [&](int tile, const int (&pg)[PPT], u32x4 (&kr)[4], u32x4 (&vr)[4], unsigned &vm) {
+    // Byte K/V: threads 0..63 also load the K scale, 64..127 the V scale, of
+    // key tid % 64 (cleared at the store past the last position: bit 4 of vm).
+    auto load_tile = [&](int tile, const int (&pg)[PPT], Raw (&kr)[4], Raw (&vr)[4], float &sr, unsigned &vm) {
         const int key0 = tile * kKeyTile;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -206,9 +243,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const bool want = key0 + kk <= last_pos;
             const bool inside = (unsigned)page < (unsigned)p.num_pages;
             bad = bad || (want && !inside);
-            kr[j] = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.k_pool +
-                                                     (size_t)(inside ? page : 0) * page_stride +
-                                                     ((size_t)g * PS + kk % PS) * kD + 8 * kg);
+            kr[j] = *reinterpret_cast<const Raw *>((const char *)p.k_pool +
+                                                   ((size_t)(inside ? page : 0) * page_stride +
+                                                    ((size_t)g * PS + kk % PS) * kD + 8 * kg) * EB);
         }
         int vpage = pg[0];
         if constexpr (PPT > 1) {
@@ -224,20 +261,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const bool want = key0 + kk <= last_pos;
             bad = bad || (want && !vinside);
             vm |= want && vinside ? 1u << j : 0u;
-            vr[j] = *reinterpret_cast<const u32x4 *>((const uint16_t *)p.v_pool +
-                                                     (size_t)(vinside ? vpage : 0) * page_stride +
-                                                     ((size_t)g * PS + kk % PS) * kD + 8 * dv);
+            vr[j] = *reinterpret_cast<const Raw *>((const char *)p.v_pool +
+                                                   ((size_t)(vinside ? vpage : 0) * page_stride +
+                                                    ((size_t)g * PS + kk % PS) * kD + 8 * dv) * EB);
+        }
+        if constexpr (kByte) {
+            const int kk = tid % 64;
+            int spage = pg[0];
+            if constexpr (PPT > 1) {
+#pragma unroll
+                for (int i = 1; i < PPT; ++i)
+                    spage = kk / PS == i ? pg[i] : spage;
+            }
+            const bool sinside = (unsigned)spage < (unsigned)p.num_pages;
+            const bool want = key0 + kk <= last_pos && sinside;
+            vm |= want ? 16u : 0u;
+            const float *src = tid < 64 ? p.k_scale : p.v_scale;
+            sr = src[((size_t)(sinside ? spage : 0) * Hkv + g) * PS + kk % PS];
         }
     };
     const int vcol = vt_column(4 * kg);
-    auto store_tile = [&](int buf, const u32x4 (&kr)[4], const u32x4 (&vraw)[4], unsigned vm) {
+    auto store_tile = [&](int buf, const Raw (&kraw)[4], const Raw (&vraw)[4], float sr, unsigned vm) {
         u32x4 vr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            vr[j] = (vm >> j) & 1u ? vraw[j] : u32x4{0u, 0u, 0u, 0u};
+            vr[j] = (vm >> j) & 1u ? widen<QT, KVT>(vraw[j]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / 16 + 16 * j) * kKStride + 8 * kg]) = kr[j];
+            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / 16 + 16 * j) * kKStride + 8 * kg]) = widen<QT, KVT>(kraw[j]);
+        if constexpr (kByte) {
+            if (tid < 128)
+                s_sc[buf][tid / 64][tid % 64] = (vm & 16u) ? sr : 0.0f;
+        }
         // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -270,16 +325,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // issued for every tile index, clamped to the last tile (whose extra copies
     // are never read), so that no branch surrounds a load or a store and the
     // waits before the stores cover exactly the loads they need.
-    u32x4 kreg[4], vreg[4];
+    Raw kreg[4], vreg[4];
+    float sreg = 0.0f;
     unsigned vmask = 0;
     int pgn[PPT];   // pages of the next tile to load
     const int last_tile = n_tiles - 1;
     if (n_tiles > 0) {
         fetch_pages(0, pgn);
-        load_tile(0, pgn, kreg, vreg, vmask);
-        store_tile(0, kreg, vreg, vmask);
+        load_tile(0, pgn, kreg, vreg, sreg, vmask);
+        store_tile(0, kreg, vreg, sreg, vmask);
         fetch_pages(min(1, last_tile), pgn);
-        load_tile(min(1, last_tile), pgn, kreg, vreg, vmask);
+        load_tile(min(1, last_tile), pgn, kreg, vreg, sreg, vmask);
         fetch_pages(min(2, last_tile), pgn);
     }
     // tile `tile` is in LDS buffer BUF; kreg / vreg hold tile + 1
@@ -288,14 +344,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // every wave is done with tile - 1 (buffer 1 - BUF), and tile's
         // stores (buffer BUF) are complete
         __syncthreads();
-        store_tile(1 - BUF, kreg, vreg, vmask);   // unread when tile + 1 is the pad tile or past it
+        store_tile(1 - BUF, kreg, vreg, sreg, vmask);   // unread when tile + 1 is the pad tile or past it
         {
             int pg[PPT];
 #pragma unroll
             for (int i = 0; i < PPT; ++i)
                 pg[i] = pgn[i];
             fetch_pages(min(tile + 3, last_tile), pgn);   // before this tile's loads
-            load_tile(min(tile + 2, last_tile), pg, kreg, vreg, vmask);
+            load_tile(min(tile + 2, last_tile), pg, kreg, vreg, sreg, vmask);
         }
 
         // ---- scores S^T[key 32 kb + 8 (j/4) + 4 h + j%4][row c] in sc[kb][j]
@@ -314,6 +370,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
             sc[KB] = x;
         });
+
+        // byte K/V: each score times its key's K scale (lane (h, c) holds keys
+        // 32 kb + 8 j4 + 4 h .. +3 in registers 4 j4 .. 4 j4 + 3)
+        if constexpr (kByte) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const float4 ks = *reinterpret_cast<const float4 *>(&s_sc[BUF][0][32 * kb + 8 * j4 + 4 * h]);
+                    sc[kb][4 * j4] *= ks.x;
+                    sc[kb][4 * j4 + 1] *= ks.y;
+                    sc[kb][4 * j4 + 2] *= ks.z;
+                    sc[kb][4 * j4 + 3] *= ks.w;
+                }
+        }
 
         // ---- online softmax of row c (log2 domain).  The causal mask is
         // needed only in tiles that reach past some valid row's position.
@@ -358,6 +429,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 ls += e;
             }
         l_run += ls;
+        // byte K/V: the probabilities that weight V carry its V scale (the sum
+        // above does not)
+        if constexpr (kByte) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const float4 vs = *reinterpret_cast<const float4 *>(&s_sc[BUF][1][32 * kb + 8 * j4 + 4 * h]);
+                    sc[kb][4 * j4] *= vs.x;
+                    sc[kb][4 * j4 + 1] *= vs.y;
+                    sc[kb][4 * j4 + 2] *= vs.z;
+                    sc[kb][4 * j4 + 3] *= vs.w;
+                }
+        }
 
         // ---- P^T operand of 16-key step ks: keys 16 ks + 4h .. +3, 16 ks + 8 + 4h .. +3
         u32x4 pb[4];
@@ -405,12 +490,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
 }
 
+template <int PS, int G, int QT>
+const void *kernel_for(int kv_dtype)
+{
+    if (kv_dtype == I8)
+        return (const void *)&paged_prefill_kernel<PS, G, QT, I8>;
+    if (kv_dtype == FP8)
+        return (const void *)&paged_prefill_kernel<PS, G, QT, FP8>;
+    return (const void *)&paged_prefill_kernel<PS, G, QT, QT>;
+}
+
 template <int PS, int G>
 int launch_g(const PrefillParams &p, dim3 grid, hipStream_t s)
 {
     void *args[] = {const_cast<PrefillParams *>(&p)};
-    const void *fn = p.q_dtype == BF16 ? (const void *)&paged_prefill_kernel<PS, G, BF16>
-                                       : (const void *)&paged_prefill_kernel<PS, G, F16>;
+    const void *fn = p.q_dtype == BF16 ? kernel_for<PS, G, BF16>(p.kv_dtype) : kernel_for<PS, G, F16>(p.kv_dtype);
     return (int)hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
 }
 
@@ -432,7 +526,7 @@ bool prefill_instantiated(int head_dim, int page_size, int group, int q_dtype, i
 {
     return head_dim == kD && (page_size == 16 || page_size == 64) &&
            (group == 1 || group == 2 || group == 4 || group == 8) && (q_dtype == F16 || q_dtype == BF16) &&
-           kv_dtype == q_dtype;
+           (kv_dtype == q_dtype || kv_dtype == I8 || kv_dtype == FP8);
 }
 
 int launch_prefill(const PrefillParams &p, int page_size, int group, void *stream)

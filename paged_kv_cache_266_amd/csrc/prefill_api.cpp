@@ -33,13 +33,16 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
     const int group = a->num_q_heads / a->num_kv_heads;
     if (!pkv::prefill_instantiated(a->head_dim, a->page_size, group, a->q_dtype, a->kv_dtype))
         return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_prefill: head_dim 128, page_size 16 or 64, group 1/2/4/8, "
-                                         "f16 or bf16 q with K/V of the same type");
+                                         "f16 or bf16 q with K/V of the same type, int8 or fp8 E4M3");
     if (a->batch == 0 || a->n_q == 0 || a->max_q_len == 0)
         return PKV_OK;
     if (!a->q || !a->k_pool || !a->v_pool || !a->block_tables || !a->q_start || !a->context_lens || !a->out)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: null device pointer");
     if ((uintptr_t)a->q % 16 || (uintptr_t)a->k_pool % 16 || (uintptr_t)a->v_pool % 16)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: q and pools must be 16-byte aligned");
+    const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
+    if (byte_kv && (!a->k_scale || !a->v_scale || (uintptr_t)a->k_scale % 4 || (uintptr_t)a->v_scale % 4))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: int8 / fp8 K/V need 4-byte aligned k_scale and v_scale");
     // one launch: grid (query blocks, KV heads, sequences)
     if (a->batch > 65535 || a->num_kv_heads > 65535)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: batch and num_kv_heads must be at most 65535");
@@ -60,6 +63,9 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
     p.max_context_len = a->max_context_len;
     p.max_q_len = a->max_q_len;
     p.q_dtype = a->q_dtype;
+    p.kv_dtype = a->kv_dtype;
+    p.k_scale = a->k_scale;
+    p.v_scale = a->v_scale;
     p.scale_log2 = a->scale * 1.4426950408889634f;
     const int err = pkv::launch_prefill(p, a->page_size, group, stream);
     return err ? launch_failed(err) : PKV_OK;

@@ -153,14 +153,15 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
 
 
 def paged_prefill(q, k_pool, v_pool, block_tables, q_start, context_lens, scale: float, *,
-                  max_context_len: int, max_q_len: int, out=None, stream=None):
+                  max_context_len: int, max_q_len: int, out=None, k_scale=None, v_scale=None, stream=None):
     """Chunked prefill attention over a paged cache.
 
     q [n_q][Hq][D] f16/bf16: sequence b's new tokens are rows
     q_start[b] .. q_start[b+1]-1 (q_start int32 [B+1], device); the pools
-    (same type as q) already hold their K/V, and context_lens [B] counts them.
-    Query i of sequence b attends to keys 0 .. context_lens[b] - nq_b + i.
-    Returns out [n_q][Hq][D] in q's type."""
+    (of q's type, or int8 / float8_e4m3fn with k_scale, v_scale
+    [num_pages][Hkv][PS] fp32) already hold their K/V, and context_lens [B]
+    counts them.  Query i of sequence b attends to keys
+    0 .. context_lens[b] - nq_b + i.  Returns out [n_q][Hq][D] in q's type."""
     import torch
 
     device = q.device
@@ -185,6 +186,12 @@ def paged_prefill(q, k_pool, v_pool, block_tables, q_start, context_lens, scale:
     a.q_dtype = DTYPE_CODES[_dtype_name(q)]
     a.kv_dtype = DTYPE_CODES[_dtype_name(k_pool)]
     a.scale = float(scale)
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is not None:
+            _check_tensor(t, n, device, 3)
+            if t.dtype != torch.float32:
+                raise TypeError(f"{n} must be float32")
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
     check(lib().pkv_paged_prefill(ctypes.byref(a), _stream_handle(stream, device)), "paged_prefill")
     return out
 

@@ -271,6 +271,9 @@ def good_prefill_args(**kw):
     (dict(out=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(k_pool=FAKE + 8), _lib.PKV_ERR_INVALID_ARG),            # not 16-byte aligned
     (dict(batch=65536, num_q_heads=8, num_kv_heads=8), _lib.PKV_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.PKV_FP8_E4M3), _lib.PKV_ERR_INVALID_ARG),                  # no scales
+    (dict(kv_dtype=_lib.PKV_I8, k_scale=FAKE), _lib.PKV_ERR_INVALID_ARG),          # no V scales
+    (dict(kv_dtype=_lib.PKV_I8, k_scale=FAKE, v_scale=FAKE + 2), _lib.PKV_ERR_INVALID_ARG),  # misaligned
 ])
 def test_prefill_rejects_bad_arguments(change, status):
     """Every check runs before the launch, so these never touch a GPU."""

@@ -54,7 +54,8 @@ def gpu_prefill(case, q_bits, q_start, dev=None, max_q_len=None, context_lens=No
     ctx = dev.context_lens if context_lens is None else torch.from_numpy(context_lens).cuda()
     mq = int(np.diff(q_start).max()) if max_q_len is None else max_q_len
     out = pkv.paged_prefill(q, dev.k_pool, dev.v_pool, dev.block_tables, qs, ctx, case.scale,
-                            max_context_len=cfg.max_context_len, max_q_len=max(mq, 1))
+                            max_context_len=cfg.max_context_len, max_q_len=max(mq, 1),
+                            k_scale=dev.k_scale, v_scale=dev.v_scale)
     torch.cuda.synchronize()
     return to_f64(out)
 
@@ -71,14 +72,16 @@ LENS = (1, 63, 64, 65, 300, 777)
 CHUNKS = (1, 63, 20, 65, 100, 130)
 
 
-@pytest.mark.parametrize("PS,G,qd", list(itertools.product((16, 64), (1, 2, 4, 8), ("f16", "bf16"))))
-def test_prefill_every_instantiation(PS, G, qd):
+@pytest.mark.parametrize("PS,G,qd,kvd", [(ps, g, qd, kvd) for ps, g, qd in itertools.product((16, 64), (1, 2, 4, 8),
+                                                                                           ("f16", "bf16"))
+                                         for kvd in (qd, "i8", "fp8")])
+def test_prefill_every_instantiation(PS, G, qd, kvd):
     """Ragged chunks: a whole 1-token sequence, a whole 63-token one, parts
     of longer ones, chunks spanning several query blocks (128/G tokens each)
-    and key tiles."""
+    and key tiles; 16-bit, int8 and E4M3 caches."""
     Hkv = 2
-    cfg = small_config(G * Hkv, Hkv, 128, qd, qd, PS, LENS)
-    note(f"[prefill] PS={PS} G={G} q={qd}")
+    cfg = small_config(G * Hkv, Hkv, 128, qd, kvd, PS, LENS)
+    note(f"[prefill] PS={PS} G={G} q={qd} kv={kvd}")
     case = make_case(cfg, seed=300 + PS + G)
     qb, qs = queries(cfg, CHUNKS, seed=PS + G)
     got = gpu_prefill(case, qb, qs)
@@ -129,8 +132,8 @@ def test_prefill_out_of_pool_page_gives_nan_rows():
     check(case, got[qs[0]:qs[1]], ref[qs[0]:qs[1]], "other sequence")
 
 
-@pytest.mark.parametrize("G,qd", [(4, "bf16"), (1, "f16")])
-def test_prefill_large_chunks_sampled_rows(G, qd):
+@pytest.mark.parametrize("G,qd,kvd", [(4, "bf16", "bf16"), (1, "f16", "f16"), (4, "bf16", "fp8"), (1, "f16", "i8")])
+def test_prefill_large_chunks_sampled_rows(G, qd, kvd):
     """16 sequences with 512-token chunks after contexts of up to 3.5k tokens
     (the chunked-context step of a long prompt): the first and last 8 rows of
     every chunk against the oracle, computed as 8-row chunks at the same
@@ -139,10 +142,10 @@ def test_prefill_large_chunks_sampled_rows(G, qd):
     chunk = 512
     lens = tuple(int(x) for x in rng.integers(chunk, 4097, size=16))
     Hkv = 8 if G == 4 else 16
-    cfg = small_config(G * Hkv, Hkv, 128, qd, qd, 64, lens)
+    cfg = small_config(G * Hkv, Hkv, 128, qd, kvd, 64, lens)
     case = make_case(cfg, seed=12)
     qb, qs = queries(cfg, (chunk,) * len(lens), seed=13)
-    note(f"[prefill large] G={G} q={qd} chunks 16 x {chunk}")
+    note(f"[prefill large] G={G} q={qd} kv={kvd} chunks 16 x {chunk}")
     got = gpu_prefill(case, qb, qs)
     last = np.concatenate([qb[qs[b + 1] - 8:qs[b + 1]] for b in range(len(lens))])
     qs8 = np.arange(0, 8 * len(lens) + 1, 8, dtype=np.int32)
