@@ -44,6 +44,11 @@
 //    V of keys past the block's last position is cleared at the store.  K is
 //    stored row-major; each thread holds four consecutive keys of eight dims
 //    of V and writes them transposed, 8 bytes per dim.
+//  * int8 / E4M3 caches: 8-byte pieces of codes, widened exactly to q's type
+//    at the LDS store (every int8 and E4M3 value is a bf16 and an f16 value);
+//    the tile's per-token K and V scales go to LDS beside it, the K scale
+//    multiplies each score and the V scale each probability that weights V
+//    (the running sum takes the probabilities without it).
 //
 // Key tiles after the block's last position are not visited.  A sequence
 // whose context length is invalid (negative, above the bound, or shorter
