@@ -3,18 +3,19 @@
 The native scheduler runs a stream of requests over a page pool.  Every step
 writes the admitted prompts' K/V and each running sequence's new token's K/V
 at the slots the scheduler hands out (pkv_write_kv, quantising f16 / bf16 rows
-into int8 / fp8 pools), then decodes the mixed batch over the block tables the
-pool builds.  Each step's output is compared with the fp64 oracle over a host
-mirror of the pools (written with the oracle's scatter and quantiser), so the
-slots, the block tables, the context lengths and the page reuse of retired
-sequences are all checked through decode.
+into int8 / fp8 pools), runs the chunked prefill of the admitted prompts (each
+prompt one chunk; head_dim 128), then decodes the mixed batch over the block
+tables the pool builds.  Each step's outputs are compared with the fp64 oracle
+over a host mirror of the pools (written with the oracle's scatter and
+quantiser), so the slots, the block tables, the context lengths and the page
+reuse of retired sequences are all checked through prefill and decode.
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import compare, note, small_config
+from gpu_helpers import TOL, compare, note, small_config, to_f64
 from synth.device import torch_dtype
 from synth.make import Case, _to_bits
 
@@ -89,8 +90,33 @@ def test_serving_loop_decodes_every_step(Hq, Hkv, D, qd, kvd, PS, policy, max_ba
             else:
                 oracle.scatter_rows(host[w], slots, rows[w])
 
+    def prefill(sids):
+        """Each admitted prompt as one chunk over its pages, against the oracle."""
+        sids = [int(x) for x in sids if prompts[int(x)] > 0]
+        if D != 128 or not sids:
+            return 0
+        lens = np.array([prompts[x] for x in sids], dtype=np.int32)
+        bt, _ = pool.block_tables(sids, cfg.max_blocks)
+        q_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        q_bits = _to_bits(rng.standard_normal((int(q_start[-1]), Hq, D)).astype(np.float32), qd)
+        out = pkv.paged_prefill(_dev16(q_bits, qd, dev), pools[0], pools[1], torch.from_numpy(bt).to(dev),
+                                torch.from_numpy(q_start).to(dev), torch.from_numpy(lens).to(dev), cfg.scale,
+                                max_context_len=cap, max_q_len=int(lens.max()), k_scale=scales[0],
+                                v_scale=scales[1])
+        torch.cuda.synchronize()
+        pcfg = small_config(Hq, Hkv, D, qd, kvd, PS, (cap,) * len(sids), num_pages=num_pages)
+        case = Case(cfg=pcfg, seed=0, context_lens=lens, free_order=np.arange(num_pages, dtype=np.int32),
+                    block_tables=bt, q_bits=np.zeros((len(sids), Hq, D), dtype=q_bits.dtype),
+                    used_pages=np.arange(num_pages, dtype=np.int32),
+                    page_index=np.arange(num_pages, dtype=np.int32), k_pages=host[0], v_pages=host[1],
+                    k_scale=host_s[0], v_scale=host_s[1], scale=cfg.scale)
+        ref = oracle.paged_prefill(case, q_bits, q_start)
+        err = float(np.abs(to_f64(out) - ref).max())
+        assert np.isfinite(to_f64(out)).all() and err <= TOL[kvd], f"prefill of {sids}: {err}"
+        return len(sids)
+
     pol = pkv.CONTINUOUS if policy == "continuous" else pkv.STATIC
-    steps = decoded = 0
+    steps = decoded = prefilled = 0
     with pkv.KVPool(num_pages, PS, initial_free_order=rng.permutation(num_pages)) as pool:
         sch = pkv.Scheduler(pool, max_batch, pol)
         arrive = 0
@@ -105,6 +131,7 @@ def test_serving_loop_decodes_every_step(Hq, Hkv, D, qd, kvd, PS, policy, max_ba
             for sid in s.admitted:
                 pages = pool.pages(int(sid))
                 write([pages[t // PS] * PS + t % PS for t in range(prompts[int(sid)])])
+            prefilled += prefill(s.admitted)
             n = len(s.seq_ids)
             if n == 0:
                 continue
@@ -132,7 +159,9 @@ def test_serving_loop_decodes_every_step(Hq, Hkv, D, qd, kvd, PS, policy, max_ba
         assert np.array_equal(got.view(host[w].dtype), host[w])
         if byte:
             assert np.array_equal(scales[w].cpu().numpy().view(np.uint32), host_s[w].view(np.uint32))
-    note(f"  {steps} steps, {decoded} sequence-steps decoded")
+    note(f"  {steps} steps, {decoded} sequence-steps decoded, {prefilled} prompts prefilled")
+    if D == 128:
+        assert prefilled > 0
 
 
 def _quiet(case, out):
