@@ -10,7 +10,8 @@
 // decode path's scaled-dot-product softmax (section 3.3 of the same page).
 //
 // Design.  One workgroup of four waves per (block of query tokens, KV head,
-// sequence).  Its 128 rows are (token, head of the group) pairs, token-major:
+// sequence), placed so that the blocks of one (sequence, KV head) run on one
+// XCD and the XCDs get an even mix of sequences.  Its 128 rows are (token, head of the group) pairs, token-major:
 // 128 / G query tokens of the G heads sharing the KV head, 32 rows per wave.
 // Both contractions run on the matrix cores as 32 x 32 products
 // (v_mfma_f32_32x32x16_{bf16,f16}: D[32][32] += A[32][16] . B[16][32]; lane
@@ -79,6 +80,7 @@ constexpr int kRows = 128;            // query rows per workgroup (4 waves x 32)
 constexpr int kD = 128;               // head_dim
 constexpr int kKStride = kD + 8;      // LDS row of K (16-bit elements), padded
 constexpr int kVStride = kKeyTile + 8;  // LDS row of transposed V (16-bit elements), padded
+constexpr unsigned kXcds = 8;         // XCDs of MI355X
 
 typedef __attribute__((ext_vector_type(2))) u32 u32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -170,8 +172,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int h = lane / 32, c = lane % 32;
-    const int qblk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+    // Work item of this workgroup.  The dispatcher deals workgroup L to XCD
+    // L mod 8.  The (sequence, KV head) pairs are dealt to the XCDs in turn
+    // (pair P to XCD P mod 8), and all query blocks of a pair go to its XCD,
+    // one after another: the blocks that re-read a pair's K/V share one L2,
+    // and every XCD gets an even mix of sequences.  Workgroups past the last
+    // pair have no work.
+    int qblk, g, b;
+    {
+        const unsigned L = blockIdx.x, x = L % kXcds, slot = L / kXcds;
+        const unsigned nqb = (unsigned)((p.max_q_len + QPB - 1) / QPB);
+        const unsigned pair = slot / nqb * kXcds + x;
+        if (pair >= (unsigned)p.batch * (unsigned)Hkv)
+            return;
+        qblk = (int)(slot % nqb);
+        g = (int)(pair % (unsigned)Hkv);
+        b = (int)(pair / (unsigned)Hkv);
+    }
 
     const int qs0 = p.q_start[b], qs1 = p.q_start[b + 1];
     if (qs0 < 0 || qs1 < qs0 || qs1 > p.n_q)
@@ -537,7 +555,11 @@ bool prefill_instantiated(int head_dim, int page_size, int group, int q_dtype, i
 int launch_prefill(const PrefillParams &p, int page_size, int group, void *stream)
 {
     const int qpb = kRows / group;
-    const dim3 grid((unsigned)((p.max_q_len + qpb - 1) / qpb), (unsigned)p.num_kv_heads, (unsigned)p.batch);
+    const size_t pairs = (size_t)p.batch * p.num_kv_heads;
+    const size_t items = (pairs + kXcds - 1) / kXcds * kXcds * (size_t)((p.max_q_len + qpb - 1) / qpb);
+    if (items > 0x7FFFFFFFu)
+        return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)items);
     hipStream_t s = (hipStream_t)stream;
     if (page_size == 16)
         return launch_ps<16>(p, group, grid, s);
