@@ -582,8 +582,9 @@ def bench_prefill(args) -> None:
     chunk of 512 new tokens at the end of its context (lengths from the
     workload's law, at least 512), the workload's K/V type.  FLOPs counted causally:
     4 * head_dim per (query row, query head, visible key).  The cpu_baseline
-    leg runs the fp64 oracle on the last 64 rows of every chunk (about 10 s
-    on 16 host cores), which is also the parity check of those rows."""
+    leg runs the fp64 oracle on the last 64 rows of every chunk (16 for an
+    E4M3 cache; about 10 s on 16 host cores), which is also the parity check
+    of those rows."""
     import numpy as np
     import torch
 
@@ -628,7 +629,8 @@ def bench_prefill(args) -> None:
 
         import oracle
 
-        nb, rows = B, 64
+        # about 10 s of fp64 work on 16 cores (E4M3 decoding makes the oracle ~4x slower per row)
+        nb, rows = B, 16 if cfg.kv_dtype == "fp8" else 64
         sub = dataclasses.replace(case, cfg=get_config(cfg.name, batch=nb, lens_kind="fixed",
                                                        lens_args=tuple(int(x) for x in lens[:nb])),
                                   context_lens=case.context_lens[:nb], block_tables=case.block_tables[:nb])
