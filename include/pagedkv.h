@@ -381,7 +381,7 @@ typedef struct pkv_prefill_args {
     int32_t n_q;                /* total query rows                                  */
     int32_t num_q_heads;
     int32_t num_kv_heads;       /* num_q_heads / num_kv_heads in {1, 2, 4, 8}        */
-    int32_t head_dim;           /* 128                                               */
+    int32_t head_dim;           /* 64 or 128                                         */
     int32_t page_size;          /* 16 or 64                                          */
     int32_t num_pages;
     int32_t max_blocks;
@@ -393,7 +393,9 @@ typedef struct pkv_prefill_args {
                                    value of a code is code x its token's scale)      */
     float scale;
     const float *k_scale;       /* device [num_pages][num_kv_heads][page_size] fp32,
-                                   4-byte aligned: int8 / fp8 K/V only, else NULL    */
+                                   4-byte aligned: int8 / fp8 K/V only, else NULL.
+                                   p.V then runs in f16: per-token V scales must stay
+                                   below ~255 or the rows become non-finite          */
     const float *v_scale;
 } pkv_prefill_args;
 

@@ -120,6 +120,7 @@ struct PrefillParams {
     int32_t max_q_len;
     int32_t q_dtype;
     int32_t kv_dtype;
+    int32_t head_dim;     // 64 or 128
     float scale_log2;     // softmax scale * log2(e)
 };
 

@@ -45,8 +45,9 @@
 //    V of keys past the block's last position is cleared at the store.  K is
 //    stored row-major; each thread holds four consecutive keys of eight dims
 //    of V and writes them transposed, 8 bytes per dim.
-//  * int8 / E4M3 caches: 8-byte pieces of codes, widened exactly to q's type
-//    at the LDS store (every int8 and E4M3 value is a bf16 and an f16 value);
+//  * int8 / E4M3 caches: 8-byte pieces of codes, widened exactly at the LDS
+//    store (every int8 and E4M3 value is a bf16 and an f16 value) -- K to
+//    q's type, V to f16, the type of the p.V product for these caches;
 //    the tile's per-token K and V scales go to LDS beside it, the K scale
 //    multiplies each score and the V scale each probability that weights V
 //    (the running sum takes the probabilities without it).
@@ -77,8 +78,6 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kKeyTile = 64;          // keys per tile
 constexpr int kRows = 128;            // query rows per workgroup (4 waves x 32)
-constexpr int kD = 128;               // head_dim
-constexpr int kKStride = kD + 8;      // LDS row of K (16-bit elements), padded
 constexpr int kVStride = kKeyTile + 8;  // LDS row of transposed V (16-bit elements), padded
 constexpr unsigned kXcds = 8;         // XCDs of MI355X
 
@@ -153,9 +152,15 @@ __device__ __forceinline__ int vt_column(int k)
     return 16 * (k / 16) + 4 * sq + k % 4;
 }
 
-template <int PS, int G, int QT, int KVT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_kernel(PrefillParams p)
+template <int D, int PS, int G, int QT, int KVT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void paged_prefill_kernel(PrefillParams p)
 {
+    constexpr int kD = D;                     // head_dim: 64 or 128
+    constexpr int kKStride = kD + 8;          // LDS row of K (16-bit elements), padded
+    constexpr int NQS = kD / 16;              // q.k steps of 16 dims
+    constexpr int NDB = kD / 32;              // 32-dim blocks of the output
+    constexpr int CPR = kD / 8;               // 16-bit 8-element chunks per K/V row
+    constexpr int NKP = kKeyTile * CPR / 256; // K pieces per thread
     constexpr int QPB = kRows / G;            // query tokens per block
     constexpr int PPT = kKeyTile / PS;        // pages per key tile
     // byte K/V (int8 or E4M3 codes with one fp32 scale per token and KV head):
@@ -163,6 +168,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     constexpr bool kByte = KVT == I8 || KVT == FP8;
     constexpr int EB = kByte ? 1 : 2;         // bytes per K/V element
     using Raw = std::conditional_t<kByte, u32x2, u32x4>;
+    // type of the p.V product: q's type for 16-bit K/V; f16 for byte K/V,
+    // whose codes are exact in f16, so that the probabilities (times the V
+    // scale) round to 11 bits instead of bf16's 8
+    constexpr int PT = kByte ? F16 : QT;
     // two buffers: tile t is read from buffer t % 2 while tile t + 1 is stored
     // into the other one
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeyTile * kKStride];
@@ -213,11 +222,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // for any finite score s below 1e22, and a masked key (-inf) still gives 0.
     const float scale = fmaxf(fabsf(p.scale_log2), 1.0e-30f);
     const u32 qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
-    u32x4 qb[8];   // B operand of step s: q[row][16s + 8h .. +8]
+    u32x4 qb[NQS];   // B operand of step s: q[row][16s + 8h .. +8]
     {
         const char *qrow = (const char *)p.q + (((size_t)(qs0 + (valid_row ? tok : i0)) * Hq + head) * kD) * 2;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < NQS; ++s) {
             const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (16 * s + 8 * h) * 2) ^ qsign;
             qb[s] = valid_row ? v : u32x4{0u, 0u, 0u, 0u};
         }
@@ -225,16 +234,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int last_pos = bad_len ? -1 : n - nq + tok_hi - 1;
     const int n_tiles = last_pos < 0 ? 0 : last_pos / kKeyTile + 1;
 
-    // ---- key-tile loads.  K: thread tid moves dims 8 (tid % 16) .. +8 of
-    // keys tid / 16 + 16 j (j < 4).  V: thread tid moves dims 8 (tid / 16) ..
-    // +8 of the four keys 4 (tid % 16) + j.
+    // ---- key-tile loads.  K: thread tid moves dims 8 (tid % CPR) .. +8 of
+    // keys tid / CPR + (256 / CPR) j (j < NKP).  V: thread tid moves dims
+    // 8 (tid / 16) .. +8 of the four keys 4 (tid % 16) + j (the threads with
+    // tid / 16 >= CPR load a duplicate and store nothing).
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
     // The block table is only read here: through the constant address space
     // its (wave-uniform) entries are scalar loads, which are counted apart
     // from the K/V loads in flight.
     typedef const __attribute__((address_space(4))) int32_t *const_i32p;
     const const_i32p bt = (const_i32p)(uintptr_t)(p.block_tables + (size_t)b * p.max_blocks);
-    const int kg = tid % 16, dv = tid / 16;
+    const int kg = tid % 16, dvt = tid / 16, dv = dvt % CPR, kc = tid % CPR;
     bool bad = false;
     // Physical pages of a tile, one per 16 or 64 keys, -1 for none.  They are
     // read one iteration before the tile's loads are issued, so that the wait
@@ -257,18 +267,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // still be NaN.
     // Byte K/V: threads 0..63 also load the K scale, 64..127 the V scale, of
     // key tid % 64 (cleared at the store past the last position: bit 4 of vm).
-    auto load_tile = [&](int tile, const int (&pg)[PPT], Raw (&kr)[4], Raw (&vr)[4], float &sr, unsigned &vm) {
+    auto load_tile = [&](int tile, const int (&pg)[PPT], Raw (&kr)[NKP], Raw (&vr)[4], float &sr, unsigned &vm) {
         const int key0 = tile * kKeyTile;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kk = tid / 16 + 16 * j;
-            const int page = pg[PPT == 1 ? 0 : j];
+        for (int j = 0; j < NKP; ++j) {
+            const int kk = tid / CPR + (256 / CPR) * j;
+            // the page of a K piece is the same across a wave: j itself at
+            // head_dim 128, one of two values per j at head_dim 64
+            int page = pg[0];
+            if constexpr (PPT > 1 && CPR == 16) {
+                page = pg[j];
+            } else if constexpr (PPT > 1) {
+                const int pi = __builtin_amdgcn_readfirstlane(kk / PS);
+#pragma unroll
+                for (int i = 1; i < PPT; ++i)
+                    page = pi == i ? pg[i] : page;
+            }
             const bool want = key0 + kk <= last_pos;
             const bool inside = (unsigned)page < (unsigned)p.num_pages;
             bad = bad || (want && !inside);
             kr[j] = *reinterpret_cast<const Raw *>((const char *)p.k_pool +
                                                    ((size_t)(inside ? page : 0) * page_stride +
-                                                    ((size_t)g * PS + kk % PS) * kD + 8 * kg) * EB);
+                                                    ((size_t)g * PS + kk % PS) * kD + 8 * kc) * EB);
         }
         int vpage = pg[0];
         if constexpr (PPT > 1) {
@@ -304,19 +324,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
     const int vcol = vt_column(4 * kg);
-    auto store_tile = [&](int buf, const Raw (&kraw)[4], const Raw (&vraw)[4], float sr, unsigned vm) {
+    auto store_tile = [&](int buf, const Raw (&kraw)[NKP], const Raw (&vraw)[4], float sr, unsigned vm) {
         u32x4 vr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            vr[j] = (vm >> j) & 1u ? widen<QT, KVT>(vraw[j]) : u32x4{0u, 0u, 0u, 0u};
+            vr[j] = (vm >> j) & 1u ? widen<PT, KVT>(vraw[j]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / 16 + 16 * j) * kKStride + 8 * kg]) = widen<QT, KVT>(kraw[j]);
+        for (int j = 0; j < NKP; ++j)
+            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / CPR + (256 / CPR) * j) * kKStride + 8 * kc]) =
+                widen<QT, KVT>(kraw[j]);
         if constexpr (kByte) {
             if (tid < 128)
                 s_sc[buf][tid / 64][tid % 64] = (vm & 16u) ? sr : 0.0f;
         }
         // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
+        if (CPR == 16 || dvt < CPR)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const u32 lo01 = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
@@ -328,9 +350,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
 
-    f32x16 oacc[4];   // O^T[dim 32 db + 8 (j/4) + 4 h + j%4][row c] in oacc[db][j]
+    f32x16 oacc[NDB];   // O^T[dim 32 db + 8 (j/4) + 4 h + j%4][row c] in oacc[db][j]
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             oacc[db][j] = 0.0f;
@@ -348,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // issued for every tile index, clamped to the last tile (whose extra copies
     // are never read), so that no branch surrounds a load or a store and the
     // waits before the stores cover exactly the loads they need.
-    Raw kreg[4], vreg[4];
+    Raw kreg[NKP], vreg[4];
     float sreg = 0.0f;
     unsigned vmask = 0;
     int pgn[PPT];   // pages of the next tile to load
@@ -386,7 +408,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             for (int j = 0; j < 16; ++j)
                 x[j] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
+            for (int s = 0; s < NQS; ++s) {
                 const u32x4 kop =
                     *reinterpret_cast<const u32x4 *>(&s_k[BUF][(32 * KB + c) * kKStride + 16 * s + 8 * h]);
                 x = mfma32<QT>(kop, qb[s], x);
@@ -436,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             l_run *= alpha;
             m_run = m_new;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     oacc[db][j] *= alpha;
@@ -472,17 +494,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kb = ks / 2, j0 = 8 * (ks % 2);
-            pb[ks] = u32x4{pack2<QT>(sc[kb][j0], sc[kb][j0 + 1]), pack2<QT>(sc[kb][j0 + 2], sc[kb][j0 + 3]),
-                           pack2<QT>(sc[kb][j0 + 4], sc[kb][j0 + 5]), pack2<QT>(sc[kb][j0 + 6], sc[kb][j0 + 7])};
+            pb[ks] = u32x4{pack2<PT>(sc[kb][j0], sc[kb][j0 + 1]), pack2<PT>(sc[kb][j0 + 2], sc[kb][j0 + 3]),
+                           pack2<PT>(sc[kb][j0 + 4], sc[kb][j0 + 5]), pack2<PT>(sc[kb][j0 + 6], sc[kb][j0 + 7])};
         }
         // ---- O^T[dim][row] += V^T[dim][key] . P^T[key][row]
-        static_for<4>([&](auto DBc) {
+        static_for<NDB>([&](auto DBc) {
             constexpr int DB = decltype(DBc)::value;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 vop =
                     *reinterpret_cast<const u32x4 *>(&s_vt[BUF][(32 * DB + c) * kVStride + 16 * ks + 8 * h]);
-                oacc[DB] = mfma32<QT>(vop, pb[ks], oacc[DB]);
+                oacc[DB] = mfma32<PT>(vop, pb[ks], oacc[DB]);
             }
         });
     };
@@ -503,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / l;
     u32x2 *orow = reinterpret_cast<u32x2 *>((uint16_t *)p.out + ((size_t)(qs0 + tok) * Hq + head) * kD);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
             // dims 32 db + 8 j4 + 4 h .. +3
@@ -513,21 +535,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
 }
 
-template <int PS, int G, int QT>
+template <int D, int PS, int G, int QT>
 const void *kernel_for(int kv_dtype)
 {
     if (kv_dtype == I8)
-        return (const void *)&paged_prefill_kernel<PS, G, QT, I8>;
+        return (const void *)&paged_prefill_kernel<D, PS, G, QT, I8>;
     if (kv_dtype == FP8)
-        return (const void *)&paged_prefill_kernel<PS, G, QT, FP8>;
-    return (const void *)&paged_prefill_kernel<PS, G, QT, QT>;
+        return (const void *)&paged_prefill_kernel<D, PS, G, QT, FP8>;
+    return (const void *)&paged_prefill_kernel<D, PS, G, QT, QT>;
+}
+
+template <int D, int PS, int G>
+const void *kernel_for_q(const PrefillParams &p)
+{
+    return p.q_dtype == BF16 ? kernel_for<D, PS, G, BF16>(p.kv_dtype) : kernel_for<D, PS, G, F16>(p.kv_dtype);
 }
 
 template <int PS, int G>
-int launch_g(const PrefillParams &p, dim3 grid, hipStream_t s)
+int launch_g(const PrefillParams &p, int head_dim, dim3 grid, hipStream_t s)
 {
     void *args[] = {const_cast<PrefillParams *>(&p)};
-    const void *fn = p.q_dtype == BF16 ? kernel_for<PS, G, BF16>(p.kv_dtype) : kernel_for<PS, G, F16>(p.kv_dtype);
+    const void *fn = head_dim == 64 ? kernel_for_q<64, PS, G>(p) : kernel_for_q<128, PS, G>(p);
     return (int)hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
 }
 
@@ -535,10 +563,10 @@ template <int PS>
 int launch_ps(const PrefillParams &p, int G, dim3 grid, hipStream_t s)
 {
     switch (G) {
-    case 1: return launch_g<PS, 1>(p, grid, s);
-    case 2: return launch_g<PS, 2>(p, grid, s);
-    case 4: return launch_g<PS, 4>(p, grid, s);
-    case 8: return launch_g<PS, 8>(p, grid, s);
+    case 1: return launch_g<PS, 1>(p, p.head_dim, grid, s);
+    case 2: return launch_g<PS, 2>(p, p.head_dim, grid, s);
+    case 4: return launch_g<PS, 4>(p, p.head_dim, grid, s);
+    case 8: return launch_g<PS, 8>(p, p.head_dim, grid, s);
     }
     return (int)hipErrorInvalidValue;
 }
@@ -547,7 +575,7 @@ int launch_ps(const PrefillParams &p, int G, dim3 grid, hipStream_t s)
 
 bool prefill_instantiated(int head_dim, int page_size, int group, int q_dtype, int kv_dtype)
 {
-    return head_dim == kD && (page_size == 16 || page_size == 64) &&
+    return (head_dim == 64 || head_dim == 128) && (page_size == 16 || page_size == 64) &&
            (group == 1 || group == 2 || group == 4 || group == 8) && (q_dtype == F16 || q_dtype == BF16) &&
            (kv_dtype == q_dtype || kv_dtype == I8 || kv_dtype == FP8);
 }
@@ -561,6 +589,8 @@ int launch_prefill(const PrefillParams &p, int page_size, int group, void *strea
         return (int)hipErrorInvalidValue;
     const dim3 grid((unsigned)items);
     hipStream_t s = (hipStream_t)stream;
+    if (p.head_dim != 64 && p.head_dim != 128)
+        return (int)hipErrorInvalidValue;
     if (page_size == 16)
         return launch_ps<16>(p, group, grid, s);
     if (page_size == 64)

@@ -32,7 +32,7 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: scale must be finite");
     const int group = a->num_q_heads / a->num_kv_heads;
     if (!pkv::prefill_instantiated(a->head_dim, a->page_size, group, a->q_dtype, a->kv_dtype))
-        return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_prefill: head_dim 128, page_size 16 or 64, group 1/2/4/8, "
+        return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_prefill: head_dim 64 or 128, page_size 16 or 64, group 1/2/4/8, "
                                          "f16 or bf16 q with K/V of the same type, int8 or fp8 E4M3");
     if (a->batch == 0 || a->n_q == 0 || a->max_q_len == 0)
         return PKV_OK;
@@ -64,6 +64,7 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
     p.max_q_len = a->max_q_len;
     p.q_dtype = a->q_dtype;
     p.kv_dtype = a->kv_dtype;
+    p.head_dim = a->head_dim;
     p.k_scale = a->k_scale;
     p.v_scale = a->v_scale;
     p.scale_log2 = a->scale * 1.4426950408889634f;

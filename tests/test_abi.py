@@ -261,7 +261,7 @@ def good_prefill_args(**kw):
     (dict(max_q_len=5000), _lib.PKV_ERR_INVALID_ARG),              # chunk longer than any context
     (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG),
     (dict(scale=float("inf")), _lib.PKV_ERR_INVALID_ARG),
-    (dict(head_dim=64), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.PKV_ERR_UNSUPPORTED),
     (dict(page_size=32, max_blocks=128), _lib.PKV_ERR_UNSUPPORTED),
     (dict(num_q_heads=48, num_kv_heads=16), _lib.PKV_ERR_UNSUPPORTED),  # group 3
     (dict(kv_dtype=_lib.PKV_F16), _lib.PKV_ERR_UNSUPPORTED),           # K/V type differs from q

@@ -72,17 +72,18 @@ LENS = (1, 63, 64, 65, 300, 777)
 CHUNKS = (1, 63, 20, 65, 100, 130)
 
 
-@pytest.mark.parametrize("PS,G,qd,kvd", [(ps, g, qd, kvd) for ps, g, qd in itertools.product((16, 64), (1, 2, 4, 8),
-                                                                                           ("f16", "bf16"))
-                                         for kvd in (qd, "i8", "fp8")])
-def test_prefill_every_instantiation(PS, G, qd, kvd):
+@pytest.mark.parametrize("D,PS,G,qd,kvd", [(d, ps, g, qd, kvd)
+                                           for d, ps, g, qd in itertools.product((64, 128), (16, 64), (1, 2, 4, 8),
+                                                                                 ("f16", "bf16"))
+                                           for kvd in (qd, "i8", "fp8")])
+def test_prefill_every_instantiation(D, PS, G, qd, kvd):
     """Ragged chunks: a whole 1-token sequence, a whole 63-token one, parts
     of longer ones, chunks spanning several query blocks (128/G tokens each)
-    and key tiles; 16-bit, int8 and E4M3 caches."""
+    and key tiles; head_dim 64 and 128; 16-bit, int8 and E4M3 caches."""
     Hkv = 2
-    cfg = small_config(G * Hkv, Hkv, 128, qd, kvd, PS, LENS)
-    note(f"[prefill] PS={PS} G={G} q={qd} kv={kvd}")
-    case = make_case(cfg, seed=300 + PS + G)
+    cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, LENS)
+    note(f"[prefill] D={D} PS={PS} G={G} q={qd} kv={kvd}")
+    case = make_case(cfg, seed=300 + PS + G + D)
     qb, qs = queries(cfg, CHUNKS, seed=PS + G)
     got = gpu_prefill(case, qb, qs)
     ref = oracle.paged_prefill(case, qb, qs)
