@@ -10,9 +10,10 @@
 // decode path's scaled-dot-product softmax (section 3.3 of the same page).
 //
 // Design.  One workgroup of four waves per (block of query tokens, KV head,
-// sequence), placed so that the blocks of one (sequence, KV head) run on one
-// XCD and the XCDs get an even mix of sequences.  Its 128 rows are (token, head of the group) pairs, token-major:
-// 128 / G query tokens of the G heads sharing the KV head, 32 rows per wave.
+// sequence), head_dim 64 or 128, placed so that the blocks of one (sequence,
+// KV head) run on one XCD and the XCDs get an even mix of sequences.  Its 128
+// rows are (token, head of the group) pairs, token-major: 128 / G query
+// tokens of the G heads sharing the KV head, 32 rows per wave.
 // Both contractions run on the matrix cores as 32 x 32 products
 // (v_mfma_f32_32x32x16_{bf16,f16}: D[32][32] += A[32][16] . B[16][32]; lane
 // l = (h, c) = (l/32, l%32) supplies A[c][8h + i] and B[8h + i][c], i < 8,
