@@ -9,10 +9,10 @@
 // sits at position n - nq + i, attending to keys 0 .. that position with the
 // decode path's scaled-dot-product softmax (section 3.3 of the same page).
 //
-// Design.  One workgroup of four waves per (block of query tokens, KV head,
+// Design.  One workgroup of eight waves per (block of query tokens, KV head,
 // sequence), head_dim 64 or 128, placed so that the blocks of one (sequence,
-// KV head) run on one XCD and the XCDs get an even mix of sequences.  Its 128
-// rows are (token, head of the group) pairs, token-major: 128 / G query
+// KV head) run on one XCD and the XCDs get an even mix of sequences.  Its 256
+// rows are (token, head of the group) pairs, token-major: 256 / G query
 // tokens of the G heads sharing the KV head, 32 rows per wave.
 // Both contractions run on the matrix cores as 32 x 32 products
 // (v_mfma_f32_32x32x16_{bf16,f16}: D[32][32] += A[32][16] . B[16][32]; lane
@@ -78,7 +78,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kKeyTile = 64;          // keys per tile
-constexpr int kRows = 128;            // query rows per workgroup (4 waves x 32)
+constexpr int kRows = 256;            // query rows per workgroup (8 waves x 32)
+constexpr int kThreads = 512;        // threads per workgroup
 constexpr int kVStride = kKeyTile + 8;  // LDS row of transposed V (16-bit elements), padded
 constexpr unsigned kXcds = 8;         // XCDs of MI355X
 
@@ -154,14 +155,14 @@ __device__ __forceinline__ int vt_column(int k)
 }
 
 template <int D, int PS, int G, int QT, int KVT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void paged_prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void paged_prefill_kernel(PrefillParams p)
 {
     constexpr int kD = D;                     // head_dim: 64 or 128
     constexpr int kKStride = kD + 8;          // LDS row of K (16-bit elements), padded
     constexpr int NQS = kD / 16;              // q.k steps of 16 dims
     constexpr int NDB = kD / 32;              // 32-dim blocks of the output
     constexpr int CPR = kD / 8;               // 16-bit 8-element chunks per K/V row
-    constexpr int NKP = kKeyTile * CPR / 256; // K pieces per thread
+    constexpr int NKP = kKeyTile * CPR / kThreads; // K pieces per thread
     constexpr int QPB = kRows / G;            // query tokens per block
     constexpr int PPT = kKeyTile / PS;        // pages per key tile
     // byte K/V (int8 or E4M3 codes with one fp32 scale per token and KV head):
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int n_tiles = last_pos < 0 ? 0 : last_pos / kKeyTile + 1;
 
     // ---- key-tile loads.  K: thread tid moves dims 8 (tid % CPR) .. +8 of
-    // keys tid / CPR + (256 / CPR) j (j < NKP).  V: thread tid moves dims
+    // keys tid / CPR + (512 / CPR) j (j < NKP).  V: thread tid moves dims
     // 8 (tid / 16) .. +8 of the four keys 4 (tid % 16) + j (the threads with
     // tid / 16 >= CPR load a duplicate and store nothing).
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
@@ -272,13 +273,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int key0 = tile * kKeyTile;
 #pragma unroll
         for (int j = 0; j < NKP; ++j) {
-            const int kk = tid / CPR + (256 / CPR) * j;
-            // the page of a K piece is the same across a wave: j itself at
-            // head_dim 128, one of two values per j at head_dim 64
+            const int kk = tid / CPR + (kThreads / CPR) * j;
             int page = pg[0];
-            if constexpr (PPT > 1 && CPR == 16) {
-                page = pg[j];
-            } else if constexpr (PPT > 1) {
+            if constexpr (PPT > 1) {
                 const int pi = __builtin_amdgcn_readfirstlane(kk / PS);
 #pragma unroll
                 for (int i = 1; i < PPT; ++i)
@@ -332,14 +329,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             vr[j] = (vm >> j) & 1u ? widen<PT, KVT>(vraw[j]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < NKP; ++j)
-            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / CPR + (256 / CPR) * j) * kKStride + 8 * kc]) =
+            *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / CPR + (kThreads / CPR) * j) * kKStride + 8 * kc]) =
                 widen<QT, KVT>(kraw[j]);
         if constexpr (kByte) {
             if (tid < 128)
                 s_sc[buf][tid / 64][tid % 64] = (vm & 16u) ? sr : 0.0f;
         }
         // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
-        if (CPR == 16 || dvt < CPR)
+        if (dvt < CPR)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const u32 lo01 = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
@@ -557,7 +554,7 @@ int launch_g(const PrefillParams &p, int head_dim, dim3 grid, hipStream_t s)
 {
     void *args[] = {const_cast<PrefillParams *>(&p)};
     const void *fn = head_dim == 64 ? kernel_for_q<64, PS, G>(p) : kernel_for_q<128, PS, G>(p);
-    return (int)hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return (int)hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, s);
 }
 
 template <int PS>

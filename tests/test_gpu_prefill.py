@@ -78,7 +78,7 @@ CHUNKS = (1, 63, 20, 65, 100, 130)
                                            for kvd in (qd, "i8", "fp8")])
 def test_prefill_every_instantiation(D, PS, G, qd, kvd):
     """Ragged chunks: a whole 1-token sequence, a whole 63-token one, parts
-    of longer ones, chunks spanning several query blocks (128/G tokens each)
+    of longer ones, chunks spanning several query blocks (256/G tokens each)
     and key tiles; head_dim 64 and 128; 16-bit, int8 and E4M3 caches."""
     Hkv = 2
     cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, LENS)
