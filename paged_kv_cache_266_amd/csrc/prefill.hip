@@ -237,16 +237,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int n_tiles = last_pos < 0 ? 0 : last_pos / kKeyTile + 1;
 
     // ---- key-tile loads.  K: thread tid moves dims 8 (tid % CPR) .. +8 of
-    // keys tid / CPR + (512 / CPR) j (j < NKP).  V: thread tid moves dims
-    // 8 (tid / 16) .. +8 of the four keys 4 (tid % 16) + j (the threads with
-    // tid / 16 >= CPR load a duplicate and store nothing).
+    // keys tid / CPR + (512 / CPR) j (j < NKP).  V: see KPT below.
     const size_t page_stride = (size_t)Hkv * PS * kD;   // elements
     // The block table is only read here: through the constant address space
     // its (wave-uniform) entries are scalar loads, which are counted apart
     // from the K/V loads in flight.
     typedef const __attribute__((address_space(4))) int32_t *const_i32p;
     const const_i32p bt = (const_i32p)(uintptr_t)(p.block_tables + (size_t)b * p.max_blocks);
-    const int kg = tid % 16, dvt = tid / 16, dv = dvt % CPR, kc = tid % CPR;
+    // V: KPT consecutive keys of 8 dims per thread -- two at head_dim 128,
+    // where the 512 threads cover the tile exactly; four at head_dim 64, where
+    // threads 0..127 do (the others load a duplicate and store nothing).
+    constexpr int KPT = CPR == 16 ? 2 : 4;
+    const int kg = KPT == 2 ? tid % 32 : tid % 16;          // key group: keys KPT kg .. +KPT
+    const int dv = KPT == 2 ? tid / 32 : (tid / 16) % CPR;  // dims 8 dv .. +8
+    const bool vstore = KPT == 2 || tid / 16 < CPR;
+    const int kc = tid % CPR;
     bool bad = false;
     // Physical pages of a tile, one per 16 or 64 keys, -1 for none.  They are
     // read one iteration before the tile's loads are issued, so that the wait
@@ -292,13 +297,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (PPT > 1) {
 #pragma unroll
             for (int i = 1; i < PPT; ++i)
-                vpage = kg / (PS / 4) == i ? pg[i] : vpage;
+                vpage = kg / (PS / KPT) == i ? pg[i] : vpage;
         }
         const bool vinside = (unsigned)vpage < (unsigned)p.num_pages;
         vm = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kk = 4 * kg + j;
+        for (int j = 0; j < KPT; ++j) {
+            const int kk = KPT * kg + j;
             const bool want = key0 + kk <= last_pos;
             bad = bad || (want && !vinside);
             vm |= want && vinside ? 1u << j : 0u;
@@ -321,11 +326,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             sr = src[((size_t)(sinside ? spage : 0) * Hkv + g) * PS + kk % PS];
         }
     };
-    const int vcol = vt_column(4 * kg);
+    const int vcol = vt_column(KPT * kg);
     auto store_tile = [&](int buf, const Raw (&kraw)[NKP], const Raw (&vraw)[4], float sr, unsigned vm) {
-        u32x4 vr[4];
+        u32x4 vr[KPT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < KPT; ++j)
             vr[j] = (vm >> j) & 1u ? widen<PT, KVT>(vraw[j]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < NKP; ++j)
@@ -335,16 +340,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (tid < 128)
                 s_sc[buf][tid / 64][tid % 64] = (vm & 16u) ? sr : 0.0f;
         }
-        // four keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high halves)
-        if (dvt < CPR)
+        // the KPT keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high
+        // halves): consecutive keys stay consecutive in a transposed row
+        if (vstore)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const u32 lo01 = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
-            const u32 lo23 = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
             const u32 hi01 = (vr[0][w] >> 16) | (vr[1][w] & 0xFFFF0000u);
-            const u32 hi23 = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
-            *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w) * kVStride + vcol]) = u32x2{lo01, lo23};
-            *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w + 1) * kVStride + vcol]) = u32x2{hi01, hi23};
+            if constexpr (KPT == 2) {
+                *reinterpret_cast<u32 *>(&s_vt[buf][(8 * dv + 2 * w) * kVStride + vcol]) = lo01;
+                *reinterpret_cast<u32 *>(&s_vt[buf][(8 * dv + 2 * w + 1) * kVStride + vcol]) = hi01;
+            } else {
+                const u32 lo23 = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
+                const u32 hi23 = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
+                *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w) * kVStride + vcol]) = u32x2{lo01, lo23};
+                *reinterpret_cast<u32x2 *>(&s_vt[buf][(8 * dv + 2 * w + 1) * kVStride + vcol]) = u32x2{hi01, hi23};
+            }
         }
     };
 
