@@ -44,8 +44,9 @@
 //    buffers, one barrier per tile), with no branch around a load or a
 //    store, so the waits before the stores cover only the loads they need.
 //    V of keys past the block's last position is cleared at the store.  K is
-//    stored row-major; each thread holds four consecutive keys of eight dims
-//    of V and writes them transposed, 8 bytes per dim.
+//    stored row-major; each thread holds consecutive keys of eight dims of V
+//    (two keys at head_dim 128, four at 64) and writes them transposed, 4 or
+//    8 bytes per dim.
 //  * int8 / E4M3 caches: 8-byte pieces of codes, widened exactly at the LDS
 //    store (every int8 and E4M3 value is a bf16 and an f16 value) -- K to
 //    q's type, V to f16, the type of the p.V product for these caches;
