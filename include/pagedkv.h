@@ -387,23 +387,28 @@ typedef struct pkv_prefill_args {
     int32_t max_blocks;
     int32_t max_context_len;    /* host bound on context_lens (<= max_blocks *
                                    page_size)                                         */
-    int32_t max_q_len;          /* host bound on every sequence's chunk length       */
+    int32_t max_q_len;          /* host bound on every sequence's chunk length; a
+                                   sequence with a longer chunk gets NaN rows where
+                                   it is written, and its rows past max_q_len are
+                                   not written at all                                */
     pkv_dtype q_dtype;          /* PKV_F16 or PKV_BF16                               */
     pkv_dtype kv_dtype;         /* == q_dtype, or PKV_I8 / PKV_FP8_E4M3 (then the
                                    value of a code is code x its token's scale)      */
     float scale;
     const float *k_scale;       /* device [num_pages][num_kv_heads][page_size] fp32,
                                    4-byte aligned: int8 / fp8 K/V only, else NULL.
-                                   p.V then runs in f16: per-token V scales must stay
-                                   below ~255 or the rows become non-finite          */
+                                   Any finite scale magnitude is handled: p.V runs
+                                   in f16 on the V scales divided by a running
+                                   power of two                                      */
     const float *v_scale;
 } pkv_prefill_args;
 
 /* Chunked prefill attention; one launch, asynchronous on `stream`.  A
  * sequence whose context length is negative, above max_context_len or shorter
- * than its chunk gets NaN rows, as does any block of rows that needs a page
- * outside the pool; rows of a sequence whose q_start entries are out of
- * order or beyond n_q are not written.  UNSUPPORTED outside the instantiated
+ * than its chunk, or whose chunk is longer than max_q_len, gets NaN rows, as
+ * does any block of rows that needs a page outside the pool; rows of a
+ * sequence whose q_start entries are out of order or beyond n_q are not
+ * written.  UNSUPPORTED outside the instantiated
  * shapes; INVALID_ARG for bad sizes (batch and num_kv_heads at most 65535
  * each) or null pointers. */
 pkv_status pkv_paged_prefill(const pkv_prefill_args *args, void *stream);

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -40,11 +41,37 @@ def common_flags() -> List[str]:
     ]
 
 
+# The compiler's per-kernel resource remarks: every kernel the library ships
+# must run without scratch (register spills to memory), which would put
+# per-lane memory traffic on the streaming loops and whose use has gone with
+# wrong results before; the build fails if any kernel needs it.
+_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+_FN = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def scratch_kernels(remarks: str) -> List[str]:
+    """Kernels whose resource remarks report a nonzero ScratchSize."""
+    bad, fn = [], None
+    for line in remarks.splitlines():
+        m = _FN.search(line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            bad.append(f"{fn} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src: str, obj: str, extra: List[str]) -> str:
-    cmd = [hipcc(), *common_flags(), *extra, "-c", "-x", "hip", src, "-o", obj]
+    cmd = [hipcc(), *common_flags(), *extra, _REMARKS, "-c", "-x", "hip", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    spills = scratch_kernels(res.stderr)
+    if spills:
+        raise RuntimeError(f"{os.path.basename(src)}: kernels use scratch memory: " + "; ".join(spills))
     return obj
 
 

@@ -146,6 +146,8 @@ static pkv_status validate(const pkv_decode_args *a, bool one_launch)
         return fail(PKV_ERR_INVALID_ARG, "decode: max_context_len exceeds max_blocks * page_size");
     if (a->num_splits < 0)
         return fail(PKV_ERR_INVALID_ARG, "decode: num_splits must be >= 0");
+    if (!std::isfinite(a->scale))
+        return fail(PKV_ERR_INVALID_ARG, "decode: scale must be finite");
     const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
     bool kv_ok = (byte_kv && (a->q_dtype == PKV_F16 || a->q_dtype == PKV_BF16)) ||
                  (a->kv_dtype == PKV_F16 && a->q_dtype == PKV_F16) ||

@@ -52,12 +52,16 @@
 //    q's type, V to f16, the type of the p.V product for these caches;
 //    the tile's per-token K and V scales go to LDS beside it, the K scale
 //    multiplies each score and the V scale each probability that weights V
-//    (the running sum takes the probabilities without it).
+//    (the running sum takes the probabilities without it).  The V scales
+//    enter as vs * 2^-e, with 2^e above every V scale seen so far, so the
+//    f16 products stay in range and normal for any scale magnitude; O is
+//    rescaled by a power of two when e grows and multiplied by 2^e at the
+//    end.
 //
 // Key tiles after the block's last position are not visited.  A sequence
-// whose context length is invalid (negative, above the bound, or shorter
-// than its chunk) gets NaN rows, as does a block that needs a page outside
-// the pool.
+// whose context length is invalid (negative, above the bound, shorter than
+// its chunk, or a chunk longer than max_q_len) gets NaN rows, as does a
+// block that needs a page outside the pool.
 
 #include <hip/hip_runtime.h>
 
@@ -179,8 +183,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // into the other one
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeyTile * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVStride];
-    // byte K/V: the tile's K scales (row 0) and V scales (row 1), per key
+    // byte K/V: the tile's K scales (row 0) and V scales (row 1), per key,
+    // and the largest V scale magnitude of the tile
     __shared__ __attribute__((aligned(16))) float s_sc[2][2][kByte ? kKeyTile : 4];
+    __shared__ float s_vmax[2];
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int h = lane / 32, c = lane % 32;
@@ -211,7 +217,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (i0 >= nq)
         return;
     const int n = p.context_lens[b];
-    const bool bad_len = n < 0 || n > p.max_context_len || nq > n;
+    // a chunk longer than max_q_len has rows no launched block covers: the
+    // blocks that do run write NaN, so the sequence is visibly invalid
+    const bool bad_len = n < 0 || n > p.max_context_len || nq > n || nq > p.max_q_len;
     const int tok_hi = min(nq, i0 + QPB);   // this block's query tokens: [i0, tok_hi)
 
     // this lane's query row: column c of the wave's 32 rows
@@ -338,8 +346,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             *reinterpret_cast<u32x4 *>(&s_k[buf][(tid / CPR + (kThreads / CPR) * j) * kKStride + 8 * kc]) =
                 widen<QT, KVT>(kraw[j]);
         if constexpr (kByte) {
+            const float sv = (vm & 16u) ? sr : 0.0f;
             if (tid < 128)
-                s_sc[buf][tid / 64][tid % 64] = (vm & 16u) ? sr : 0.0f;
+                s_sc[buf][tid / 64][tid % 64] = sv;
+            if (wave == 1) {
+                // threads 64..127 (one wave) hold the tile's V scales
+                float m = fabsf(sv);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1)
+                    m = fmaxf(m, __shfl_xor(m, o));
+                if (lane == 0)
+                    s_vmax[buf] = m;
+            }
         }
         // the KPT keys of dims 8 dv + 2 w (low halves) and 8 dv + 2 w + 1 (high
         // halves): consecutive keys stay consecutive in a transposed row
@@ -373,6 +391,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // sum, scaled by the same stale reference, still give O / sum exactly.
     constexpr float kSlack = 8.0f;
     float m_run = -3.0e38f, l_run = 0.0f;
+    // Byte K/V: the probabilities that weight V are multiplied by the key's V
+    // scale and rounded to f16 for the p.V product.  To keep that product in
+    // f16's normal range whatever the scales' magnitude, the V scales are
+    // applied as vs * 2^-e_run, with 2^e_run above every V scale seen so far
+    // (e_run only grows, tile by tile; O is rescaled by a power of two, an
+    // exact step, when it does), and the output is O * 2^e_run / sum.  The V
+    // scales of a tile are the same for every row, so e_run is uniform over
+    // the workgroup.  kNoExp: no nonzero V scale seen yet (O is zero).
+    constexpr int kNoExp = -1000;
+    int e_run = kNoExp;
 
     // One register set carries tile t + 1 from its loads (issued while tile
     // t - 1 is computed) to its LDS store (before tile t is computed); the
@@ -484,18 +512,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 ls += e;
             }
         l_run += ls;
-        // byte K/V: the probabilities that weight V carry its V scale (the sum
-        // above does not)
+        // byte K/V: the probabilities that weight V carry its V scale times
+        // 2^-e_run (the sum above takes neither)
         if constexpr (kByte) {
+            const float vmax = s_vmax[BUF];
+            // 2^e_tile > vmax: the biased exponent of vmax minus 126
+            const int e_tile = vmax > 0.0f ? (int)((__builtin_bit_cast(u32, vmax) >> 23) & 0xFFu) - 126 : kNoExp;
+            if (e_tile > e_run) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        oacc[db][j] = ldexpf(oacc[db][j], max(e_run - e_tile, -300));
+                e_run = e_tile;
+            }
+            const float f = e_run == kNoExp ? 0.0f : ldexpf(1.0f, -e_run);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
                     const float4 vs = *reinterpret_cast<const float4 *>(&s_sc[BUF][1][32 * kb + 8 * j4 + 4 * h]);
-                    sc[kb][4 * j4] *= vs.x;
-                    sc[kb][4 * j4 + 1] *= vs.y;
-                    sc[kb][4 * j4 + 2] *= vs.z;
-                    sc[kb][4 * j4 + 3] *= vs.w;
+                    sc[kb][4 * j4] *= vs.x * f;
+                    sc[kb][4 * j4 + 1] *= vs.y * f;
+                    sc[kb][4 * j4 + 2] *= vs.z * f;
+                    sc[kb][4 * j4 + 3] *= vs.w * f;
                 }
         }
 
@@ -533,6 +573,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!valid_row)
         return;
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / l;
+    // byte K/V: O was accumulated in units of 2^e_run
+    const int e_out = kByte && e_run != kNoExp ? e_run : 0;
+    auto fin = [&](float x) { return kByte ? ldexpf(x * inv, e_out) : x * inv; };
     u32x2 *orow = reinterpret_cast<u32x2 *>((uint16_t *)p.out + ((size_t)(qs0 + tok) * Hq + head) * kD);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -540,8 +583,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j4 = 0; j4 < 4; ++j4) {
             // dims 32 db + 8 j4 + 4 h .. +3
             const int j = 4 * j4;
-            orow[(32 * db + 8 * j4 + 4 * h) / 4] = u32x2{pack2<QT>(oacc[db][j] * inv, oacc[db][j + 1] * inv),
-                                                        pack2<QT>(oacc[db][j + 2] * inv, oacc[db][j + 3] * inv)};
+            orow[(32 * db + 8 * j4 + 4 * h) / 4] = u32x2{pack2<QT>(fin(oacc[db][j]), fin(oacc[db][j + 1])),
+                                                        pack2<QT>(fin(oacc[db][j + 2]), fin(oacc[db][j + 3]))};
         }
 }
 

@@ -38,8 +38,10 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_prefill_args *a, void *stream)
         return PKV_OK;
     if (!a->q || !a->k_pool || !a->v_pool || !a->block_tables || !a->q_start || !a->context_lens || !a->out)
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: null device pointer");
-    if ((uintptr_t)a->q % 16 || (uintptr_t)a->k_pool % 16 || (uintptr_t)a->v_pool % 16)
-        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: q and pools must be 16-byte aligned");
+    if ((uintptr_t)a->q % 16 || (uintptr_t)a->k_pool % 16 || (uintptr_t)a->v_pool % 16 || (uintptr_t)a->out % 16)
+        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: q, pools and out must be 16-byte aligned");
+    if (((uintptr_t)a->block_tables & 3u) || ((uintptr_t)a->q_start & 3u) || ((uintptr_t)a->context_lens & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: int32 arrays must be 4-byte aligned");
     const bool byte_kv = a->kv_dtype == PKV_I8 || a->kv_dtype == PKV_FP8_E4M3;
     if (byte_kv && (!a->k_scale || !a->v_scale || (uintptr_t)a->k_scale % 4 || (uintptr_t)a->v_scale % 4))
         return fail(PKV_ERR_INVALID_ARG, "pkv_paged_prefill: int8 / fp8 K/V need 4-byte aligned k_scale and v_scale");

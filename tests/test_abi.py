@@ -86,6 +86,9 @@ def test_valid_arguments_pass_validation():
     (dict(max_context_len=4097), _lib.PKV_ERR_INVALID_ARG),      # > max_blocks * page_size
     (dict(batch=-1), _lib.PKV_ERR_INVALID_ARG),
     (dict(num_splits=-1), _lib.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG),        # non-finite scale
+    (dict(scale=float("inf")), _lib.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), _lib.PKV_ERR_INVALID_ARG),
     (dict(workspace=None), _lib.PKV_ERR_WORKSPACE),
     (dict(workspace_bytes=16), _lib.PKV_ERR_WORKSPACE),
 ])
@@ -270,6 +273,8 @@ def good_prefill_args(**kw):
     (dict(q_start=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(out=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(k_pool=FAKE + 8), _lib.PKV_ERR_INVALID_ARG),            # not 16-byte aligned
+    (dict(out=FAKE + 8), _lib.PKV_ERR_INVALID_ARG),               # out not 16-byte aligned
+    (dict(q_start=FAKE + 2), _lib.PKV_ERR_INVALID_ARG),           # int32 array misaligned
     (dict(batch=65536, num_q_heads=8, num_kv_heads=8), _lib.PKV_ERR_INVALID_ARG),
     (dict(kv_dtype=_lib.PKV_FP8_E4M3), _lib.PKV_ERR_INVALID_ARG),                  # no scales
     (dict(kv_dtype=_lib.PKV_I8, k_scale=FAKE), _lib.PKV_ERR_INVALID_ARG),          # no V scales

@@ -1,0 +1,234 @@
+"""GPU tests of documented contracts at their edges, a seeded random sweep of
+the supported shapes, and back-to-back reuse of one workspace (needs a
+gfx950 GPU).
+
+Every check compares the HIP path, called through the C ABI, with the fp64
+oracle or with the path's own first result, and stops at the first
+mismatch."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, compare, gpu_decode, note, small_config, to_f64
+from synth import make_case
+from synth.device import torch_dtype, upload
+from synth.make import _to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_266_amd as pkv
+
+    pkv.lib()
+    yield
+
+
+# ---------------------------------------------------------------------------
+# Decode: a context length below 0 or above max_context_len gives NaN for
+# that sequence (nothing is read for it), 0 gives zeros, and every other
+# sequence of the same batch still matches the oracle.
+
+@pytest.mark.parametrize("D,G,qd,kvd,PS", [(128, 4, "bf16", "bf16", 64), (64, 2, "f16", "f16", 16),
+                                           (128, 1, "f16", "i8", 16), (128, 4, "bf16", "fp8", 64),
+                                           (64, 8, "bf16", "fp8", 16)])
+def test_decode_invalid_lengths_give_nan_for_that_sequence_only(D, G, qd, kvd, PS):
+    import torch
+
+    lens = (300, 200, 777, 64, 150, 1)
+    Hkv = 2
+    cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, lens)
+    case = make_case(cfg, seed=61 + D + G)
+    ref = oracle.paged_decode(case)
+    dev = upload(case, "cuda")
+    bad = torch.tensor([300, -5, 777, cfg.max_context_len + 10, 0, -2 ** 31], dtype=torch.int32, device="cuda")
+    note(f"[invalid lengths] D={D} G={G} q={qd} kv={kvd} PS={PS} lens {bad.tolist()}")
+    for splits in (0, 3, 40):
+        d = dataclasses.replace(dev, context_lens=bad)
+        g = to_f64(gpu_decode(case, num_splits=splits, dev=d))
+        assert np.isnan(g[1]).all() and np.isnan(g[3]).all() and np.isnan(g[5]).all(), splits
+        assert (g[4] == 0).all(), splits
+        for b in (0, 2):
+            err = np.abs(g[b] - ref[b]).max()
+            assert err <= TOL[kvd], (splits, b, err)
+
+
+# ---------------------------------------------------------------------------
+# int8 / E4M3 caches whose V scales are far from 1: the outputs scale with
+# the V scales, so the error against the oracle, divided by the factor, must
+# stay within the usual bound -- for tiny scales (the f16 products of the
+# prefill would be subnormal without its power-of-two normalisation) and
+# large ones (they would overflow f16).  Along each sequence the V scales of
+# page j are also multiplied by 2^-(3 - j % 4) (so the largest scale seen
+# grows over the first four pages and the prefill's running exponent is
+# raised mid-sequence) and by a per-token jitter in [0.75, 1].
+
+def _rescaled(case, factor, seed):
+    rng = np.random.default_rng(seed)
+    vs = case.v_scale * np.float32(factor) * rng.uniform(0.75, 1.0, size=case.v_scale.shape).astype(np.float32)
+    nblk = -(-case.context_lens // case.cfg.page_size)
+    for b in range(case.cfg.batch):
+        for j in range(int(nblk[b])):
+            row = case.page_index[case.block_tables[b, j]]
+            vs[row] *= np.float32(2.0 ** -(3 - j % 4))
+    return dataclasses.replace(case, v_scale=vs.astype(np.float32))
+
+
+def _prefill_queries(cfg, chunks, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(sum(chunks)), cfg.num_q_heads, cfg.head_dim)).astype(np.float32)
+    return _to_bits(q, cfg.q_dtype), np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+
+
+def _prefill(case, qb, qs, max_q_len=None, out=None, context_lens=None):
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    cfg = case.cfg
+    dev = upload(case, "cuda")
+    q = torch.from_numpy(np.ascontiguousarray(qb).view(np.int16)).view(torch_dtype(cfg.q_dtype)).cuda()
+    ctx = dev.context_lens if context_lens is None else torch.from_numpy(context_lens).cuda()
+    mq = int(np.diff(qs).max()) if max_q_len is None else max_q_len
+    res = pkv.paged_prefill(q, dev.k_pool, dev.v_pool, dev.block_tables, torch.from_numpy(qs).cuda(), ctx,
+                            case.scale, max_context_len=cfg.max_context_len, max_q_len=mq, out=out,
+                            k_scale=dev.k_scale, v_scale=dev.v_scale)
+    torch.cuda.synchronize()
+    return to_f64(res)
+
+
+@pytest.mark.parametrize("kvd,qd,factor", [(kvd, qd, f) for kvd, qd in (("i8", "f16"), ("fp8", "bf16"),
+                                                                        ("i8", "bf16"), ("fp8", "f16"))
+                                             for f in (1e-6, 1e-3, 1e5 if qd == "bf16" else 2e3)])
+def test_byte_cache_scale_magnitudes(kvd, qd, factor):
+    """(The large factor is 2e3 for f16 outputs, whose range ends at 65504.)"""
+    cfg = small_config(8, 2, 128, qd, kvd, 64, (300, 777, 1000))
+    case = _rescaled(make_case(cfg, seed=71), factor, seed=72)
+    note(f"[scale magnitudes] kv={kvd} q={qd} V scales x{factor:g}")
+    qb, qs = _prefill_queries(cfg, (100, 200, 130), seed=73)
+    got = _prefill(case, qb, qs)
+    ref = oracle.paged_prefill(case, qb, qs)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max() / factor
+    note(f"  prefill: max|err| / factor {err:.3e} (tol {TOL[kvd]})")
+    assert err <= TOL[kvd]
+    # decode over the same cache keeps fp32 products: the same bound
+    ref_d = oracle.paged_decode(case)
+    for splits in (0, 5):
+        g = to_f64(gpu_decode(case, num_splits=splits))
+        assert np.isfinite(g).all()
+        err_d = np.abs(g - ref_d).max() / factor
+        note(f"  decode splits={splits}: max|err| / factor {err_d:.3e}")
+        assert err_d <= TOL[kvd]
+
+
+# ---------------------------------------------------------------------------
+# Prefill: a chunk longer than max_q_len gets NaN in the rows the launched
+# blocks cover and leaves its rows past max_q_len untouched; the other
+# sequences are unaffected.
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_prefill_chunk_longer_than_max_q_len(G):
+    import torch
+
+    cfg = small_config(2 * G, 2, 128, "bf16", "bf16", 16, (300, 90, 600))
+    case = make_case(cfg, seed=81)
+    qpb = 256 // G                # query tokens per block
+    chunks = (10, 30, 2 * qpb + 38)
+    qb, qs = _prefill_queries(cfg, chunks, seed=82)
+    ref = oracle.paged_prefill(case, qb, qs)
+    max_q_len = qpb + 5           # two query blocks are launched per sequence; the third chunk needs three
+    out = torch.full((int(qs[-1]), cfg.num_q_heads, cfg.head_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+    note(f"[prefill max_q_len] G={G} chunks {chunks} max_q_len {max_q_len}")
+    got = _prefill(case, qb, qs, max_q_len=max_q_len, out=out)
+    covered = 2 * qpb
+    s2 = got[qs[2]:qs[3]]
+    assert np.isnan(s2[:covered]).all()
+    assert (s2[covered:] == 7.0).all()
+    for b in (0, 1):
+        assert np.abs(got[qs[b]:qs[b + 1]] - ref[qs[b]:qs[b + 1]]).max() <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# A seeded random sweep over the supported set: head_dim, page size, group,
+# dtype pair, KV heads, batch, ragged lengths (empty, single-token, page and
+# tile boundaries, a few thousand tokens), and wave counts.  Each case is
+# compared element by element with the oracle; the sweep stops at the first
+# mismatch and prints the case that failed.
+
+def _fuzz_case(rng, i):
+    D = int(rng.choice([64, 128]))
+    PS = int(rng.choice([16, 64]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    qd, kvd = [("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"),
+               ("f16", "fp8"), ("bf16", "fp8")][int(rng.integers(6))]
+    Hkv = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 13))
+    pool = [0, 1, PS - 1, PS, PS + 1, 63, 64, 65, 127, 128, 129]
+    lens = tuple(int(rng.choice(pool)) if rng.random() < 0.4 else int(rng.integers(1, 3000)) for _ in range(B))
+    if max(lens) == 0:
+        lens = lens[:-1] + (1,)
+    splits = int(rng.choice([0, 1, 2, 3, int(rng.integers(4, 300))]))
+    return D, PS, G, qd, kvd, Hkv, lens, splits
+
+
+def test_random_sweep_against_oracle():
+    rng = np.random.default_rng(2026)
+    for i in range(60):
+        D, PS, G, qd, kvd, Hkv, lens, splits = _fuzz_case(rng, i)
+        note(f"[sweep {i}] D={D} PS={PS} G={G} q={qd} kv={kvd} Hkv={Hkv} splits={splits} lens={lens}")
+        cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, lens)
+        case = make_case(cfg, seed=1000 + i, poison=bool(i % 3 == 0))
+        compare(case, gpu_decode(case, num_splits=splits), f"sweep {i}")
+
+
+# ---------------------------------------------------------------------------
+# 200 back-to-back one-launch calls on one workspace and one counter array,
+# with many segments shared by several waves (the in-kernel merge on every
+# call): every output is bitwise equal to the first, the first matches the
+# oracle, and the counters are zero at the end.
+
+def test_merge_soak_200_calls_bitwise():
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    lens = (20000, 9, 20000, 3000, 65, 12000, 777, 40000)
+    cfg = small_config(32, 8, 128, "bf16", "bf16", 64, lens)
+    case = make_case(cfg, seed=91)
+    dev = upload(case, "cuda")
+    out = torch.empty_like(dev.q)
+    a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                        max_context_len=cfg.max_context_len, out=out, num_splits=700)
+    ws = pkv.alloc_workspace(a, "cuda")
+    ctr = pkv.alloc_merge_counters(a, "cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    a.merge_counters, a.merge_counter_bytes = ctr.data_ptr(), 4 * ctr.numel()
+    sh = torch.cuda.current_stream().cuda_stream
+    note("[soak] 200 calls, 700 waves, 8 sequences up to 40k tokens")
+    check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+    torch.cuda.synchronize()
+    first = out.clone()
+    compare(case, first, "first call")
+    same = torch.ones((), dtype=torch.bool, device="cuda")
+    for i in range(199):
+        check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+        same &= (out.view(torch.int16) == first.view(torch.int16)).all()
+        if i % 50 == 49:
+            torch.cuda.synchronize()
+            note(f"  {i + 2} calls")
+            assert bool(same), f"output differs from the first call by call {i + 2}"
+    torch.cuda.synchronize()
+    assert bool(same)
+    assert int(ctr.abs().sum()) == 0
