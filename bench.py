@@ -39,7 +39,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--config", default=None,
+                    help="one decode workload (default: every decode workload, headline first, in one line)")
+    ap.add_argument("--flush-check", action="store_true",
+                    help="with --config: also time one layer with a 512 MiB scratch write between launches")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --config: also time the launches replayed from a HIP graph")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="waves sharing the batch's tiles (0 = library default)")
     ap.add_argument("--rotate", type=int, default=0,
@@ -685,56 +690,40 @@ def bench_prefill(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
-def main():
-    args = parse()
-    if args.summarize_counters:
-        from synth import CONFIGS, make_case
+GATED = ("llama3_8b_gqa", "long_128k")     # >= 70 % of the HBM peak on one GPU
+GATE_FRAC = 0.70
+# the default run: the headline workload first, then the other gated one,
+# the rest of the decode workloads, and the launch-bound tiny case
+SUITE = ("llama3_8b_gqa", "long_128k", "llama2_7b_mha", "qwen_1p8b_int8", "llama3_8b_gqa_fp8", "tiny")
+SECONDARY_CPU_SECONDS = 4.0                # oracle sample of each non-headline workload
+FLUSH_MIB = 512                            # scratch written between launches in the cache-flush check
+FLUSH_TOLERANCE = 0.03
 
-        rec = summarize_counters(args.config, args.summarize_counters, COPY_CALIBRATION_MIB << 20)
-        rec["bytes_alg_per_launch"] = make_case(CONFIGS[args.config]).bytes_alg()
-        rec["traffic_over_alg"] = round(rec["hbm_bytes_per_launch"] / rec["bytes_alg_per_launch"], 4)
-        path = os.path.join(ROOT, "profiles", f"paged_decode_{args.config}_counters.json")
-        os.makedirs(os.path.dirname(path), exist_ok=True)
-        with open(path, "w") as f:
-            json.dump(rec, f, indent=1)
-            f.write("\n")
-        print(json.dumps(rec))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_workload(name: str, args, cpu_seconds: float, flush_check: bool = False, graph: bool = False) -> dict:
+    """Benchmark one decode workload: W warm-up steps, K timed steps (one
+    library call, one kernel launch each) between synchronisations, layers
+    rotated so that >= 1 GB of KV cycles.  Returns its record: wall time per
+    step, the kernel's roofline (HIP events on the launch stream around the K
+    launches), the parity of the first launch against the fp64 oracle and the
+    oracle's own throughput on this host (cpu_seconds of work)."""
+    import ctypes
 
     import numpy as np
     import torch
-
-    if args.copy_calibration:
-        copy_calibration(COPY_CALIBRATION_MIB)
-        return
-    if args.stream_reference:
-        stream_reference(2048)
-        return
-    if args.op == "append":
-        bench_append(args)
-        return
-    if args.op == "serve":
-        bench_serve(args)
-        return
-    if args.op == "prefill":
-        bench_prefill(args)
-        return
 
     import paged_kv_cache_266_amd as pkv
     from paged_kv_cache_266_amd._lib import check, lib
     from synth import CONFIGS, make_case
     from synth.device import upload
-    import ctypes
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     L = lib()
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[name]
+    t_set = time.perf_counter()
     case = make_case(cfg)
     bytes_alg = case.bytes_alg()
 
@@ -745,7 +734,8 @@ def main():
         bt, lens = pool.block_tables(list(range(cfg.batch)), cfg.max_blocks)
     assert (bt == case.block_tables).all() and (lens == case.context_lens).all()
 
-    kv_bytes_layer = case.total_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * (1 if cfg.kv_dtype in ("i8", "fp8") else 2)
+    kv_bytes_layer = case.total_tokens * cfg.num_kv_heads * cfg.head_dim * 2 * \
+        (1 if cfg.kv_dtype in ("i8", "fp8") else 2)
     rotate = args.rotate or max(1, -(-(1 << 30) // max(kv_bytes_layer, 1)))
     layers = [upload(case, "cuda") for _ in range(rotate)]
     q = layers[0].q
@@ -768,14 +758,10 @@ def main():
         a.merge_counters = 0 if ctr is None else ctr.data_ptr()
         a.merge_counter_bytes = 0 if ctr is None else 4 * ctr.numel()
     num_splits = L.pkv_decode_num_splits(ctypes.byref(argv[0]))
+    launch_bound = name == "tiny"
 
     def step(i):
         check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
-
-    def step_timed(i, ev):
-        ev[0].record(stream)
-        check(L.pkv_paged_attn_decode(ctypes.byref(argv[i % rotate]), sh))
-        ev[1].record(stream)
 
     # the cpu_baseline leg (which also checks the first launch's output) runs
     # first: the oracle keeps the GPU idle for seconds, so it must not sit
@@ -786,7 +772,8 @@ def main():
     tol = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}[cfg.kv_dtype]
     parity, baseline = {"ok": None, "note": "not checked: --no-cpu-baseline"}, None
     if not args.no_cpu_baseline:
-        parity, baseline = cpu_baseline(case, args.cpu_seconds, got, tol)
+        parity, baseline = cpu_baseline(case, cpu_seconds, got, tol)
+    log(f"[{name}] set-up and oracle leg {time.perf_counter() - t_set:.1f} s")
 
     # W warm-up steps, then more (untimed) until the GPU has been busy for
     # WARMUP_SECONDS, so that clocks have settled before the timed region
@@ -818,16 +805,21 @@ def main():
     # a second pass of K steps with an event pair around each launch: the
     # spread of launch durations (each pair adds its own overhead, so these
     # read a little above the timed region's average)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step_timed(args.warmup + args.steps + i, evs[i])
-    torch.cuda.synchronize()
-    kern_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    def per_launch_ms(n, between=None):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for k in range(n):
+            if between is not None:
+                between()
+            evs[k][0].record(stream)
+            step(args.warmup + args.steps + k)
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
+    kern_ms = per_launch_ms(args.steps)
     achieved = bytes_alg / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(cfg.name)
-    result = {
+    rec = {
         "metric": "paged-attn decode HBM GB/s (% of 8 TB/s peak), us per layer-step",
         "value": round(value, 2),
         "unit": "GB/s",
@@ -857,20 +849,182 @@ def main():
             "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
             "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
         },
-        "roofline": {
+        "roofline": None if launch_bound else {
             "bound": "hbm",
             "kernel": decode_kernel_name(cfg.name),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
+            "traffic": traffic_from_profile(cfg.name),
         },
         "parity": parity,
-        "source_digest": source_digest(),
     }
+    if launch_bound:
+        rec["note"] = "launch-bound: a few KB per step, no roofline claim"
     if baseline is not None:
-        result["cpu_baseline"] = baseline
+        rec["cpu_baseline"] = baseline
+
+    if flush_check:
+        # Cross-check of the rotation: one layer only, with FLUSH_MIB of
+        # scratch streamed through the caches between launches so no K/V byte
+        # can come from them; per-launch event pairs on both sides (like with
+        # like).  The flush READS the scratch (a reduction): a flush that
+        # writes it leaves dirty lines whose write-back then competes with the
+        # decode's reads, which times the write-back rather than the decode
+        # (reported beside it for that reason).
+        scratch = torch.ones((FLUSH_MIB << 20) // 4, dtype=torch.float32, device="cuda")
+        one = argv[0]
+
+        def flushed(n, flush):
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+            torch.cuda.synchronize()
+            for k in range(n):
+                flush(k)
+                evs[k][0].record(stream)
+                check(L.pkv_paged_attn_decode(ctypes.byref(one), sh))
+                evs[k][1].record(stream)
+            torch.cuda.synchronize()
+            return np.array([e[0].elapsed_time(e[1]) for e in evs])
+
+        sink = torch.empty((), dtype=torch.float32, device="cuda")
+        read_flush = lambda k: torch.sum(scratch, out=sink)          # noqa: E731
+        write_flush = lambda k: scratch.fill_(float(k))               # noqa: E731
+        flushed(3, read_flush)
+        med_r = float(np.median(kern_ms)) * 1e3
+        med_f = float(np.median(flushed(args.steps, read_flush))) * 1e3
+        med_w = float(np.median(flushed(args.steps, write_flush))) * 1e3
+        rec["flush_cross_check"] = {
+            "flush_mib": FLUSH_MIB, "layers": 1, "flush": "read (reduction)",
+            "kernel_event_us_median": round(med_f, 2),
+            "rotation_kernel_event_us_median": round(med_r, 2), "layers_rotated": rotate,
+            "rel_diff": round(med_f / med_r - 1.0, 4),
+            "flagged": bool(abs(med_f / med_r - 1.0) > FLUSH_TOLERANCE),
+            "write_flush_kernel_event_us_median": round(med_w, 2),
+        }
+        del scratch, sink
+
+    if graph:
+        # the launch overhead apart: the same launches captured in a HIP graph
+        # (K decode launches, no memset nodes) and replayed; every replay's
+        # output is checked against the eager output, bit for bit
+        ref_out = out.clone()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            for k in range(args.steps):
+                check(L.pkv_paged_attn_decode(ctypes.byref(argv[k % rotate]), cap.cuda_stream))
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        same = True
+        for _ in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            same = same and bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
+            step(0)                                   # eager work between replays
+            torch.cuda.synchronize()
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ge[0].record(stream)
+        reps = 10
+        for _ in range(reps):
+            g.replay()
+        ge[1].record(stream)
+        torch.cuda.synchronize()
+        rec["graph_replay"] = {"launches_per_graph": args.steps, "replays": reps,
+                               "us_per_layer_step": round(ge[0].elapsed_time(ge[1]) * 1e3 / (reps * args.steps), 2),
+                               "outputs_bit_exact": same,
+                               "note": "beside the stream-launched number above, never in place of it"}
+        del g
+    del layers, argv, ws, ctr, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def compact(rec: dict) -> dict:
+    """A secondary workload's record inside the headline line."""
+    keep = ("value", "unit", "ms_per_step", "us_per_layer_step", "pct_of_peak", "kernel_us_timed_region",
+            "kernel_event_us", "roofline", "parity", "cpu_baseline", "graph_replay", "note")
+    out = {k: rec[k] for k in keep if k in rec}
+    c = rec["config"]
+    out["config"] = {k: c[k] for k in ("batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "q_dtype",
+                                       "kv_dtype", "context_tokens", "num_splits", "layers_rotated", "seed",
+                                       "bytes_alg_per_step")}
+    return out
+
+
+def main():
+    args = parse()
+    if args.summarize_counters:
+        from synth import CONFIGS, make_case
+
+        name = args.config or DEFAULT_CONFIG
+        rec = summarize_counters(name, args.summarize_counters, COPY_CALIBRATION_MIB << 20)
+        rec["bytes_alg_per_launch"] = make_case(CONFIGS[name]).bytes_alg()
+        rec["traffic_over_alg"] = round(rec["hbm_bytes_per_launch"] / rec["bytes_alg_per_launch"], 4)
+        path = os.path.join(ROOT, "profiles", f"paged_decode_{name}_counters.json")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(COPY_CALIBRATION_MIB)
+        return
+    if args.stream_reference:
+        stream_reference(2048)
+        return
+    if args.op != "decode" and args.config is None:
+        args.config = DEFAULT_CONFIG
+    if args.op == "append":
+        bench_append(args)
+        return
+    if args.op == "serve":
+        bench_serve(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
+        return
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.config is not None:
+        # one workload (profiling runs, sweeps)
+        rec = decode_workload(args.config, args, args.cpu_seconds, flush_check=args.flush_check,
+                              graph=args.graph or args.config == "tiny")
+        rec["source_digest"] = source_digest()
+        print(json.dumps(rec), flush=True)
+        return
+
+    # the default run: every decode workload, the headline's record on top
+    recs = {}
+    for name in SUITE:
+        head = name == DEFAULT_CONFIG
+        recs[name] = decode_workload(name, args, args.cpu_seconds if head else min(args.cpu_seconds,
+                                                                                  SECONDARY_CPU_SECONDS),
+                                     flush_check=head, graph=name == "tiny")
+        r = recs[name]
+        log(f"[{name}] {r['us_per_layer_step']} us/step, {r['value']} GB/s"
+            + (f", roofline frac {r['roofline']['frac']}" if r["roofline"] else "")
+            + f", parity {r['parity'].get('ok')}")
+    result = recs[DEFAULT_CONFIG]
+    result["gate"] = {"threshold_frac": GATE_FRAC,
+                      "workloads": {n: {"frac": recs[n]["roofline"]["frac"],
+                                        "parity_ok": recs[n]["parity"].get("ok"),
+                                        "pass": bool(recs[n]["roofline"]["frac"] >= GATE_FRAC
+                                                     and recs[n]["parity"].get("ok"))} for n in GATED}}
+    result["workloads"] = {n: compact(recs[n]) for n in SUITE if n != DEFAULT_CONFIG}
+    result["source_digest"] = source_digest()
     print(json.dumps(result), flush=True)
 
 

@@ -107,9 +107,11 @@ def _prefill(case, qb, qs, max_q_len=None, out=None, context_lens=None):
 
 @pytest.mark.parametrize("kvd,qd,factor", [(kvd, qd, f) for kvd, qd in (("i8", "f16"), ("fp8", "bf16"),
                                                                         ("i8", "bf16"), ("fp8", "f16"))
-                                             for f in (1e-6, 1e-3, 1e5 if qd == "bf16" else 2e3)])
+                                             for f in ((1e-6, 1e-3, 1e5) if qd == "bf16" else (1e-3, 2e3))])
 def test_byte_cache_scale_magnitudes(kvd, qd, factor):
-    """(The large factor is 2e3 for f16 outputs, whose range ends at 65504.)"""
+    """Outputs have q's type, so for f16 the factors keep them inside f16's
+    normal range (above 6.1e-5, below 65504): an f16 output near 1e-6 is a
+    subnormal with a few bits, whatever the kernel computes."""
     cfg = small_config(8, 2, 128, qd, kvd, 64, (300, 777, 1000))
     case = _rescaled(make_case(cfg, seed=71), factor, seed=72)
     note(f"[scale magnitudes] kv={kvd} q={qd} V scales x{factor:g}")
