@@ -290,6 +290,22 @@ pkv_status pkv_paged_attn_decode(const pkv_decode_args *args, void *stream);
 pkv_status pkv_paged_attn_decode_partitions(const pkv_decode_args *args, void *stream);
 pkv_status pkv_splitk_reduce(const pkv_decode_args *args, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * pkv_paged_attn_decode with the workspace and merge counters taken from a
+ * static device array of the library instead of the caller.  `workspace`,
+ * `workspace_bytes`, `merge_counters` and `merge_counter_bytes` of args are
+ * ignored; everything else is as for pkv_paged_attn_decode, with the same
+ * result.  The array holds 32 MiB of workspace and 1 MiB of counters:
+ * shapes whose pkv_decode_workspace_bytes or pkv_decode_counter_bytes exceed
+ * that return PKV_ERR_WORKSPACE (nothing launched).  Each GPU the library
+ * runs on holds its own array until the process ends; the first call on a
+ * device looks up its address and enqueues one small kernel that zeroes the
+ * counters.  No call allocates or frees memory.  All calls on one GPU share
+ * the array, so calls that may overlap in time on one GPU (two streams, two
+ * threads) race and give wrong results; serialise them. */
+pkv_status pkv_paged_attn_decode_noalloc(const pkv_decode_args *args, void *stream);
+
 /* ===================================================================== *
  * Device: write appended tokens' K/V into their slots (the device side of
  * append_tokens, section 3.1 of the first page).

@@ -34,7 +34,7 @@ EXPORTED = [
     "pkv_decode_workspace_bytes", "pkv_decode_counter_bytes", "pkv_decode_num_splits",
     "pkv_decode_validate",
     "pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
-    "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
+    "pkv_paged_attn_decode_noalloc", "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
     "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
     "pkv_sched_get_stats", "pkv_sched_batch_tables", "pkv_paged_prefill",
 ]
@@ -193,7 +193,8 @@ def _declare(L):
     L.pkv_decode_num_splits.argtypes = [P(DecodeArgs)]
     L.pkv_decode_validate.restype = ci
     L.pkv_decode_validate.argtypes = [P(DecodeArgs)]
-    for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce"):
+    for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
+                 "pkv_paged_attn_decode_noalloc"):
         getattr(L, name).restype = ci
         getattr(L, name).argtypes = [P(DecodeArgs), vp]
     L.pkv_write_kv.restype = ci

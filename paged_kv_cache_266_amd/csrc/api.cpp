@@ -16,6 +16,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -131,8 +132,9 @@ static uint32_t next_tag()
     return t;
 }
 
-// Shape, dtype and pointer checks; no GPU access.
-static pkv_status validate(const pkv_decode_args *a, bool one_launch)
+// Shape, dtype and pointer checks of everything but the workspace and the
+// merge counters; no GPU access.
+static pkv_status validate_core(const pkv_decode_args *a)
 {
     if (!a)
         return fail(PKV_ERR_INVALID_ARG, "decode: null argument struct");
@@ -168,6 +170,16 @@ static pkv_status validate(const pkv_decode_args *a, bool one_launch)
         ((uintptr_t)a->block_tables & 3u) || ((uintptr_t)a->context_lens & 3u))
         return fail(PKV_ERR_INVALID_ARG, "decode: q, pools and out must be 16-byte aligned, "
                                          "scales and int32 arrays 4-byte aligned");
+    return PKV_OK;
+}
+
+// validate_core, then the workspace (and, for the one-launch form, the merge
+// counters) the caller passed.
+static pkv_status validate(const pkv_decode_args *a, bool one_launch)
+{
+    const pkv_status st = validate_core(a);
+    if (st != PKV_OK || a->batch == 0)
+        return st;
     const size_t need = workspace_bytes(a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need || ((uintptr_t)a->workspace & 255u)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace missing, smaller than "
@@ -317,6 +329,91 @@ extern "C" pkv_status pkv_paged_attn_decode(const pkv_decode_args *a, void *stre
     int err = launch_decode_partitions(p, a->head_dim, a->page_size, a->num_q_heads / a->num_kv_heads,
                                        a->q_dtype, a->kv_dtype, stream);
     return err ? device_fail(err, "pkv_paged_attn_decode") : PKV_OK;
+}
+
+// ---- decode for callers that cannot allocate --------------------------------
+//
+// pkv_paged_attn_decode_noalloc keeps its workspace and merge counters in
+// `scratch`, a file-scope device array: every GPU the library runs on holds
+// its own copy, at its own address, until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// the device address is looked up once per device, at the entry point's first
+// call there, and kept in g_scratch.
+
+constexpr size_t kNoAllocWorkspaceBytes = (size_t)32 << 20;
+constexpr size_t kNoAllocCounterBytes = (size_t)1 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocWorkspaceBytes + kNoAllocCounterBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static char *g_scratch[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, uint32_t n)
+{
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u)
+        p[i] = 0u;
+}
+
+// Device address of this device's scratch.  On the first call for a device
+// the merge counters are cleared (static device memory starts zeroed and
+// every complete call leaves the counters zero, so this is belt and braces)
+// by a kernel on `stream`, ahead of the decode launch that follows.
+static pkv_status scratch_for_current_device(hipStream_t stream, char **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return device_fail((int)e, "pkv_paged_attn_decode_noalloc");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_ERR_DEVICE, "pkv_paged_attn_decode_noalloc: device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return device_fail((int)(e != hipSuccess ? e : hipErrorInvalidSymbol),
+                               "pkv_paged_attn_decode_noalloc: hipGetSymbolAddress");
+        char *base = (char *)ptr;
+        hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream,
+                           (uint32_t *)(base + kNoAllocWorkspaceBytes), (uint32_t)(kNoAllocCounterBytes / 4));
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return device_fail((int)e, "pkv_paged_attn_decode_noalloc: clearing the merge counters");
+        g_scratch[dev] = base;
+    }
+    *out = g_scratch[dev];
+    return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_noalloc(const pkv_decode_args *a, void *stream)
+{
+    clear_error();
+    pkv_status st = validate_core(a);
+    if (st != PKV_OK || a->batch == 0)
+        return st;
+    const size_t need = workspace_bytes(a), need_ctr = counter_bytes(a);
+    if (need > kNoAllocWorkspaceBytes || need_ctr > kNoAllocCounterBytes) {
+        char buf[256];
+        std::snprintf(buf, sizeof buf,
+                      "pkv_paged_attn_decode_noalloc: these shapes need %zu bytes of workspace and %zu of merge "
+                      "counters; the static scratch holds %zu and %zu",
+                      need, need_ctr, kNoAllocWorkspaceBytes, kNoAllocCounterBytes);
+        return fail(PKV_ERR_WORKSPACE, buf);
+    }
+    char *base = nullptr;
+    st = scratch_for_current_device((hipStream_t)stream, &base);
+    if (st != PKV_OK)
+        return st;
+    pkv_decode_args b = *a;
+    b.workspace = base;
+    b.workspace_bytes = kNoAllocWorkspaceBytes;
+    b.merge_counters = (uint32_t *)(base + kNoAllocWorkspaceBytes);
+    b.merge_counter_bytes = kNoAllocCounterBytes;
+    DecodeParams p = make_params(&b);
+    p.fused = 1;
+    int err = launch_decode_partitions(p, b.head_dim, b.page_size, b.num_q_heads / b.num_kv_heads, b.q_dtype,
+                                       b.kv_dtype, stream);
+    return err ? device_fail(err, "pkv_paged_attn_decode_noalloc") : PKV_OK;
 }
 
 extern "C" pkv_status pkv_write_kv(const pkv_write_args *a, void *stream)

@@ -295,3 +295,19 @@ def test_prefill_empty_work_is_a_no_op():
         a = good_prefill_args(q=None, k_pool=None, v_pool=None, out=None, **change)
         assert L.pkv_paged_prefill(ctypes.byref(a), None) == _lib.PKV_OK, change
     assert L.pkv_paged_prefill(None, None) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_shapes_beyond_its_scratch():
+    """pkv_paged_attn_decode_noalloc: a batch whose workspace would exceed the
+    library's static scratch is refused before any device work, with a
+    message naming the sizes; bad arguments get the same codes as the
+    allocating entry point."""
+    L = _lib.lib()
+    a = good_args(batch=60000, num_q_heads=64, num_kv_heads=8, workspace=None, workspace_bytes=0,
+                  merge_counters=None, merge_counter_bytes=0)
+    assert L.pkv_paged_attn_decode_noalloc(ctypes.byref(a), None) == _lib.PKV_ERR_WORKSPACE
+    assert "static scratch" in L.pkv_last_error().decode()
+    for change, code in ((dict(head_dim=96), _lib.PKV_ERR_UNSUPPORTED), (dict(q=None), _lib.PKV_ERR_INVALID_ARG),
+                         (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG)):
+        assert L.pkv_paged_attn_decode_noalloc(ctypes.byref(good_args(**change)), None) == code, change
+    assert L.pkv_paged_attn_decode_noalloc(ctypes.byref(good_args(batch=0, q=None)), None) == _lib.PKV_OK
