@@ -66,6 +66,9 @@ def parse():
                                                               "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this benchmark and "
                          "of the copy calibration into profiles/paged_decode_<config>_counters.json")
+    ap.add_argument("--sq-counters", nargs="*", metavar="CSV", default=[],
+                    help="with --summarize-counters: further rocprofv3 --pmc CSVs of the same workload (SQ_*, "
+                         "GRBM_* and derived counters such as VALUBusy), averaged per decode dispatch")
     return ap.parse_args()
 
 
@@ -145,6 +148,38 @@ def summarize_counters(workload: str, files, copy_bytes: int) -> dict:
         "hbm_write_bytes_per_launch": int(write_b),
         "hbm_bytes_per_launch": int(fetch_b + write_b),
     }
+
+
+def summarize_sq(files) -> dict:
+    """Per-dispatch means of every counter in the given rocprofv3 --pmc CSVs
+    for the decode kernel's dispatches, and the ratios read from them: the
+    fraction of wave cycles spent waiting for an instruction's operands
+    (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES), vector-ALU and vector-memory
+    instructions per wave, and the matrix-core instruction count."""
+    import csv
+
+    sums, counts = {}, {}
+    for path in files:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if "paged_decode_" not in r["Kernel_Name"]:
+                    continue
+                k = r["Counter_Name"]
+                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    mean = {k: sums[k] / counts[k] for k in sums}
+    out = {"per_dispatch_mean": {k: round(v, 3) for k, v in sorted(mean.items())},
+           "dispatches": {k: counts[k] for k in sorted(counts)}}
+    waves = mean.get("SQ_WAVES")
+    ratios = {}
+    if "SQ_WAIT_INST_ANY" in mean and mean.get("SQ_WAVE_CYCLES"):
+        ratios["wait_inst_any_over_wave_cycles"] = round(mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"], 4)
+    if waves:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            if k in mean:
+                ratios[k.lower().replace("sq_insts_", "insts_") + "_per_wave"] = round(mean[k] / waves, 1)
+    out["ratios"] = ratios
+    return out
 
 
 def copy_calibration(mib: int) -> None:
@@ -888,7 +923,7 @@ def decode_workload(name: str, args, cpu_seconds: float, flush_check: bool = Fal
             return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
         sink = torch.empty((), dtype=torch.float32, device="cuda")
-        read_flush = lambda k: torch.sum(scratch, out=sink)          # noqa: E731
+        read_flush = lambda k: torch.sum(scratch, dim=0, out=sink)   # noqa: E731
         write_flush = lambda k: scratch.fill_(float(k))               # noqa: E731
         flushed(3, read_flush)
         med_r = float(np.median(kern_ms)) * 1e3
@@ -963,6 +998,8 @@ def main():
         rec = summarize_counters(name, args.summarize_counters, COPY_CALIBRATION_MIB << 20)
         rec["bytes_alg_per_launch"] = make_case(CONFIGS[name]).bytes_alg()
         rec["traffic_over_alg"] = round(rec["hbm_bytes_per_launch"] / rec["bytes_alg_per_launch"], 4)
+        if args.sq_counters:
+            rec["sq"] = summarize_sq(args.sq_counters)
         path = os.path.join(ROOT, "profiles", f"paged_decode_{name}_counters.json")
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as f:
