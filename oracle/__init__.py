@@ -32,10 +32,19 @@ SRC_PATH = os.path.join(HERE, "oracle.c")
 DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "fp8": 3}
 
 
-def build(verbose: bool = False, src: str = SRC_PATH, out: str = LIB_PATH) -> str:
-    """Compile the oracle with gcc (always recompiles)."""
+# An alternative oracle build to load instead of liboracle.so (the
+# sanitizer build of the tests).
+LIBRARY_ENV = "PKV_ORACLE_LIBRARY"
+SANITIZE_FLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, src: str = SRC_PATH, out: str = LIB_PATH, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (always recompiles); with sanitize, an
+    AddressSanitizer + UndefinedBehaviorSanitizer build (load it with the ASan
+    runtime preloaded and PKV_ORACLE_LIBRARY=<out>)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter",
+           "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter", *(SANITIZE_FLAGS if sanitize else []),
            src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
@@ -81,6 +90,8 @@ def load(path: str):
 
 def lib():
     global _lib
+    if _lib is None and os.environ.get(LIBRARY_ENV):
+        _lib = load(os.environ[LIBRARY_ENV])
     if _lib is None:
         if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
             build()

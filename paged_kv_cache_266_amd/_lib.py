@@ -39,6 +39,20 @@ EXPORTED = [
     "pkv_sched_get_stats", "pkv_sched_batch_tables", "pkv_paged_prefill",
 ]
 
+# The host-only build (page pool, scheduler, status codes; no GPU entry
+# points): the sanitizer build of the host code loads it through the
+# PKV_HOST_LIBRARY environment variable instead of libpagedkv.so.
+HOST_EXPORTED = [
+    "pkv_abi_version", "pkv_status_string", "pkv_last_error",
+    "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_alloc", "pkv_append_tokens",
+    "pkv_seq_release", "pkv_seq_info", "pkv_seq_pages", "pkv_free_page_count",
+    "pkv_free_pages", "pkv_build_block_tables", "pkv_kv_bytes",
+    "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners",
+    "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
+    "pkv_sched_get_stats", "pkv_sched_batch_tables",
+]
+HOST_LIBRARY_ENV = "PKV_HOST_LIBRARY"
+
 PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC = 0, 1
 
 
@@ -154,81 +168,67 @@ _EXC = {PKV_ERR_OOM: KVCacheOOM, PKV_ERR_NO_SEQ: UnknownSequence,
 _lib = None
 
 
-def _declare(L):
+def _signatures():
     i32, i64, sz, vp, ci = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
     P = ctypes.POINTER
-    L.pkv_abi_version.restype = i32
-    L.pkv_abi_version.argtypes = []
-    L.pkv_status_string.restype = ctypes.c_char_p
-    L.pkv_status_string.argtypes = [ci]
-    L.pkv_last_error.restype = ctypes.c_char_p
-    L.pkv_last_error.argtypes = []
-    L.pkv_device_count.restype = i32
-    L.pkv_device_count.argtypes = []
-    L.pkv_pool_create.restype = ci
-    L.pkv_pool_create.argtypes = [P(PoolDesc), P(vp)]
-    L.pkv_pool_destroy.restype = None
-    L.pkv_pool_destroy.argtypes = [vp]
-    L.pkv_seq_alloc.restype = ci
-    L.pkv_seq_alloc.argtypes = [vp, i64, i32, P(i64)]
-    L.pkv_append_tokens.restype = ci
-    L.pkv_append_tokens.argtypes = [vp, i64, i32, P(i64)]
-    L.pkv_seq_release.restype = ci
-    L.pkv_seq_release.argtypes = [vp, i64]
-    L.pkv_seq_info.restype = ci
-    L.pkv_seq_info.argtypes = [vp, i64, P(i32), P(i32)]
-    L.pkv_seq_pages.restype = ci
-    L.pkv_seq_pages.argtypes = [vp, i64, P(i32), i32, P(i32)]
-    L.pkv_free_page_count.restype = i32
-    L.pkv_free_page_count.argtypes = [vp]
-    L.pkv_free_pages.restype = ci
-    L.pkv_free_pages.argtypes = [vp, P(i32), i32, P(i32)]
-    L.pkv_build_block_tables.restype = ci
-    L.pkv_build_block_tables.argtypes = [vp, P(i64), i32, i32, P(i32), P(i32)]
-    L.pkv_kv_bytes.restype = i64
-    L.pkv_kv_bytes.argtypes = [i32, i32, i32, i64, i32, ci]
-    L.pkv_decode_workspace_bytes.restype = ci
-    L.pkv_decode_workspace_bytes.argtypes = [P(DecodeArgs), P(sz)]
-    L.pkv_decode_num_splits.restype = i32
-    L.pkv_decode_num_splits.argtypes = [P(DecodeArgs)]
-    L.pkv_decode_validate.restype = ci
-    L.pkv_decode_validate.argtypes = [P(DecodeArgs)]
+    sig = {
+        "pkv_abi_version": (i32, []),
+        "pkv_status_string": (ctypes.c_char_p, [ci]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_device_count": (i32, []),
+        "pkv_pool_create": (ci, [P(PoolDesc), P(vp)]),
+        "pkv_pool_destroy": (None, [vp]),
+        "pkv_seq_alloc": (ci, [vp, i64, i32, P(i64)]),
+        "pkv_append_tokens": (ci, [vp, i64, i32, P(i64)]),
+        "pkv_seq_release": (ci, [vp, i64]),
+        "pkv_seq_info": (ci, [vp, i64, P(i32), P(i32)]),
+        "pkv_seq_pages": (ci, [vp, i64, P(i32), i32, P(i32)]),
+        "pkv_free_page_count": (i32, [vp]),
+        "pkv_free_pages": (ci, [vp, P(i32), i32, P(i32)]),
+        "pkv_build_block_tables": (ci, [vp, P(i64), i32, i32, P(i32), P(i32)]),
+        "pkv_kv_bytes": (i64, [i32, i32, i32, i64, i32, ci]),
+        "pkv_decode_workspace_bytes": (ci, [P(DecodeArgs), P(sz)]),
+        "pkv_decode_counter_bytes": (ci, [P(DecodeArgs), P(sz)]),
+        "pkv_decode_num_splits": (i32, [P(DecodeArgs)]),
+        "pkv_decode_validate": (ci, [P(DecodeArgs)]),
+        "pkv_write_kv": (ci, [P(WriteArgs), vp]),
+        "pkv_seq_fork": (ci, [vp, i64, i64]),
+        "pkv_append_tokens_cow": (ci, [vp, i64, i32, P(i64), P(i32), P(i32)]),
+        "pkv_page_owners": (i32, [vp, i32]),
+        "pkv_copy_pages": (ci, [P(CopyArgs), vp]),
+        "pkv_sched_create": (ci, [vp, i32, ci, P(vp)]),
+        "pkv_sched_destroy": (None, [vp]),
+        "pkv_sched_submit": (ci, [vp, i64, i32, i32, i64]),
+        "pkv_sched_finish": (ci, [vp, i64]),
+        "pkv_sched_step": (ci, [vp, i32, P(i64), P(i64), P(i32), P(i64), P(i64), P(SchedStepOut)]),
+        "pkv_paged_prefill": (ci, [P(PrefillArgs), vp]),
+        "pkv_sched_batch_tables": (ci, [vp, i32, i32, P(i32), P(i32), P(i32)]),
+        "pkv_sched_get_stats": (ci, [vp, P(SchedStats)]),
+    }
     for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
                  "pkv_paged_attn_decode_noalloc"):
-        getattr(L, name).restype = ci
-        getattr(L, name).argtypes = [P(DecodeArgs), vp]
-    L.pkv_write_kv.restype = ci
-    L.pkv_write_kv.argtypes = [P(WriteArgs), vp]
-    L.pkv_seq_fork.restype = ci
-    L.pkv_seq_fork.argtypes = [vp, i64, i64]
-    L.pkv_append_tokens_cow.restype = ci
-    L.pkv_append_tokens_cow.argtypes = [vp, i64, i32, P(i64), P(i32), P(i32)]
-    L.pkv_page_owners.restype = i32
-    L.pkv_page_owners.argtypes = [vp, i32]
-    L.pkv_copy_pages.restype = ci
-    L.pkv_copy_pages.argtypes = [P(CopyArgs), vp]
-    L.pkv_sched_create.restype = ci
-    L.pkv_sched_create.argtypes = [vp, i32, ci, P(vp)]
-    L.pkv_sched_destroy.restype = None
-    L.pkv_sched_destroy.argtypes = [vp]
-    L.pkv_sched_submit.restype = ci
-    L.pkv_sched_submit.argtypes = [vp, i64, i32, i32, i64]
-    L.pkv_sched_finish.restype = ci
-    L.pkv_sched_finish.argtypes = [vp, i64]
-    L.pkv_sched_step.restype = ci
-    L.pkv_sched_step.argtypes = [vp, i32, P(i64), P(i64), P(i32), P(i64), P(i64), P(SchedStepOut)]
-    L.pkv_paged_prefill.restype = ci
-    L.pkv_paged_prefill.argtypes = [P(PrefillArgs), vp]
-    L.pkv_sched_batch_tables.restype = ci
-    L.pkv_sched_batch_tables.argtypes = [vp, i32, i32, P(i32), P(i32), P(i32)]
-    L.pkv_sched_get_stats.restype = ci
-    L.pkv_sched_get_stats.argtypes = [vp, P(SchedStats)]
+        sig[name] = (ci, [P(DecodeArgs), vp])
+    return sig
+
+
+def _declare(L, host_only: bool = False):
+    for name, (res, args) in _signatures().items():
+        if host_only and name not in HOST_EXPORTED:
+            continue
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
     return L
 
 
 def lib():
-    """Load libpagedkv.so (raises if it has not been built)."""
+    """Load libpagedkv.so (raises if it has not been built).  With
+    PKV_HOST_LIBRARY set, load that host-only build instead: only the pool,
+    scheduler and status entry points exist then, and any device call fails
+    with AttributeError."""
     global _lib
+    if _lib is None and os.environ.get(HOST_LIBRARY_ENV):
+        _lib = _declare(ctypes.CDLL(os.environ[HOST_LIBRARY_ENV]), host_only=True)
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(

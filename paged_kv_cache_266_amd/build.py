@@ -21,7 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["decode.hip", "api.cpp", "pool.cpp", "sched.cpp", "prefill.hip", "prefill_api.cpp"]
+SOURCES = ["decode.hip", "api.cpp", "errors.cpp", "pool.cpp", "sched.cpp", "prefill.hip", "prefill_api.cpp"]
+# the host-only part (page pool, scheduler, status codes): plain C++, no HIP
+HOST_SOURCES = ["errors.cpp", "pool.cpp", "sched.cpp"]
 
 
 def hipcc() -> str:
@@ -93,6 +95,24 @@ def build(verbose: bool = False, extra_flags: Optional[List[str]] = None) -> str
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host(out: str, sanitize: bool = True) -> str:
+    """The host-only part of the library (page pool, scheduler, status codes)
+    as a plain C++ shared library built by g++, with AddressSanitizer and
+    UndefinedBehaviorSanitizer by default.  It exports the pool and scheduler
+    entry points of include/pagedkv.h and nothing that touches a GPU; load it
+    with PKV_HOST_LIBRARY=<out> and the ASan runtime preloaded."""
+    srcs = [os.path.join(CSRC, s) for s in HOST_SOURCES]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-Wall", f"-I{os.path.join(ROOT, 'include')}",
+           *(SANITIZE_FLAGS if sanitize else []), *srcs, "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"host build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return out
 
 
 if __name__ == "__main__":

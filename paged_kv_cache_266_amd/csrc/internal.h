@@ -7,17 +7,9 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/pagedkv.h"
+#include "host.h"
 
 namespace pkv {
-
-// Thread-local error message behind pkv_last_error().
-void clear_error();
-pkv_status fail(pkv_status code, const char *msg);
-
-// Pool geometry, for the scheduler.
-int32_t pool_page_size(const pkv_pool *pool);
-int32_t pool_num_pages(const pkv_pool *pool);
 
 // Tokens per wave-iteration of the decode kernel.
 constexpr int kTileTokens = 64;

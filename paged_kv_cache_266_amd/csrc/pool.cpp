@@ -17,7 +17,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "internal.h"
+#include "host.h"
 
 struct pkv_pool {
     int32_t num_pages = 0;

@@ -17,7 +17,7 @@
 #include <unordered_set>
 #include <vector>
 
-#include "internal.h"
+#include "host.h"
 
 namespace {
 
