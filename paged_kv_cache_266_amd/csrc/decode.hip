@@ -407,13 +407,59 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane)
     return x;
 }
 
+// Context lengths of the first kLensRegs * 64 sequences, held in registers
+// (lane l of register i: sequence 64 i + l; 0 past the batch), all loaded
+// at once at the start of a wave: the wave's location in the batch, its
+// first tile and every later segment change then need no further load of
+// context_lens (one round trip to memory instead of a dependent chain of
+// them, also spared by every wave at once on the same two cache lines).
+// Sequences beyond them are read from memory.
+constexpr int kLensRegs = 4;
+
+struct Lens {
+    // four named registers (not an array: an array captured by the kernels'
+    // lambdas can be left in scratch memory instead of registers)
+    int v0, v1, v2, v3;
+
+    __device__ __forceinline__ void load(const DecodeParams &p, int lane)
+    {
+        auto at = [&](int b) { return b < p.batch ? p.context_lens[b] : 0; };
+        v0 = at(lane);
+        v1 = at(64 + lane);
+        v2 = at(128 + lane);
+        v3 = at(192 + lane);
+    }
+
+    // this lane's register of chunk i (i < kLensRegs, wave-uniform)
+    __device__ __forceinline__ int reg(int i) const { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
+
+    // context length of sequence b (wave-uniform b, 0 <= b < batch)
+    __device__ __forceinline__ int of(const DecodeParams &p, int b) const
+    {
+        if (b >= 64 * kLensRegs)
+            return p.context_lens[b];
+        return __builtin_amdgcn_readlane(reg(b / 64), b & 63);
+    }
+
+    // context lengths of sequences c .. c+63 (c a multiple of 64), lane l
+    // holding sequence c + l (0 past the batch)
+    __device__ __forceinline__ int chunk(const DecodeParams &p, int c, int lane) const
+    {
+        if (c >= 64 * kLensRegs) {
+            const int b = c + lane;
+            return b < p.batch ? p.context_lens[b] : 0;
+        }
+        return reg(c / 64);
+    }
+};
+
 // Tiles of one KV head over the whole batch.
-__device__ __forceinline__ int batch_tiles(const DecodeParams &p, int lane)
+__device__ __forceinline__ int batch_tiles(const DecodeParams &p, const Lens &lens, int lane)
 {
     int total = 0;
     for (int c = 0; c < p.batch; c += 64) {
         const int b = c + lane;
-        total += wave_sum_int(b < p.batch ? tiles_of(p.context_lens[b], p.max_context_len) : 0);
+        total += wave_sum_int(b < p.batch ? tiles_of(lens.chunk(p, c, lane), p.max_context_len) : 0);
     }
     return total;
 }
@@ -432,14 +478,14 @@ __device__ __forceinline__ long long owner_of(long long t, long long T, long lon
 
 // Sequence containing global tile t (t < total) and the first global tile of
 // that sequence: walks the batch 64 sequences at a time.
-__device__ __forceinline__ void locate(const DecodeParams &p, long long t, int lane, int &b_out,
+__device__ __forceinline__ void locate(const DecodeParams &p, const Lens &lens, long long t, int lane, int &b_out,
                                        long long &start_out)
 {
     int carry = 0;
     const int Hkv = p.num_kv_heads;
     for (int c = 0; c < p.batch; c += 64) {
         const int b = c + lane;
-        const int nt = b < p.batch ? tiles_of(p.context_lens[b], p.max_context_len) : 0;
+        const int nt = b < p.batch ? tiles_of(lens.chunk(p, c, lane), p.max_context_len) : 0;
         const int incl = wave_incl_scan(nt, lane);
         const bool past = b < p.batch && (long long)(carry + incl) * Hkv > t;
         const unsigned long long mask = __ballot(past);
@@ -602,11 +648,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
     const long long NW = gridDim.x, w = blockIdx.x;
 
-    const long long T = (long long)batch_tiles(p, lane) * Hkv;
+    Lens lens;
+    lens.load(p, lane);
+    const long long T = (long long)batch_tiles(p, lens, lane) * Hkv;
     // a sequence without tiles (empty, or an invalid length) has no wave
     // streaming it: its outputs are written here, zeros (NaN if invalid)
     for (long long b = w; b < p.batch; b += NW) {
-        const int n = p.context_lens[b];
+        const int n = lens.of(p, (int)b);
         if (tiles_of(n, p.max_context_len) == 0) {
             const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
             u32 *o = reinterpret_cast<u32 *>(p.out) + (size_t)b * Hq * D / 2;
@@ -638,8 +686,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     Cursor cur;
     {
         long long start;
-        locate(p, lo, lane, cur.b, start);
-        cur.n = p.context_lens[cur.b];
+        locate(p, lens, lo, lane, cur.b, start);
+        cur.n = lens.of(p, cur.b);
         cur.nt = tiles_of(cur.n, p.max_context_len);
         const long long off = lo - start;
         cur.g = (int)(off / cur.nt);
@@ -656,7 +704,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 // only advances while tiles of its range remain)
                 do {
                     ++x.b;
-                    x.n = x.b < p.batch ? p.context_lens[x.b] : 0;
+                    x.n = x.b < p.batch ? lens.of(p, x.b) : 0;
                     x.nt = tiles_of(x.n, p.max_context_len);
                 } while (x.nt == 0 && x.b < p.batch);
             }
@@ -1180,9 +1228,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
     const long long NW = gridDim.x, w = blockIdx.x;
 
-    const long long T = (long long)batch_tiles(p, lane) * Hkv;
+    Lens lens;
+    lens.load(p, lane);
+    const long long T = (long long)batch_tiles(p, lens, lane) * Hkv;
     for (long long b = w; b < p.batch; b += NW) {
-        const int n = p.context_lens[b];
+        const int n = lens.of(p, (int)b);
         if (tiles_of(n, p.max_context_len) == 0) {
             const float fill = (n < 0 || n > p.max_context_len) ? __builtin_nanf("") : 0.0f;
             u32 *o = reinterpret_cast<u32 *>(p.out) + (size_t)b * Hq * D / 2;
@@ -1211,8 +1261,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     Cursor cur;
     {
         long long start;
-        locate(p, lo, lane, cur.b, start);
-        cur.n = p.context_lens[cur.b];
+        locate(p, lens, lo, lane, cur.b, start);
+        cur.n = lens.of(p, cur.b);
         cur.nt = tiles_of(cur.n, p.max_context_len);
         const long long off = lo - start;
         cur.g = (int)(off / cur.nt);
@@ -1227,7 +1277,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
                 x.g = 0;
                 do {
                     ++x.b;
-                    x.n = x.b < p.batch ? p.context_lens[x.b] : 0;
+                    x.n = x.b < p.batch ? lens.of(p, x.b) : 0;
                     x.nt = tiles_of(x.n, p.max_context_len);
                 } while (x.nt == 0 && x.b < p.batch);
             }
