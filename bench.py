@@ -401,15 +401,17 @@ def bench_append(args) -> None:
 
 
 def bench_serve(args) -> None:
-    """The serving loop over one layer's pools: each step runs the native
-    scheduler (retire, admit, one token per running sequence), writes the
-    admitted prompts' K/V and every new token's K/V at their slots, builds the
-    block tables, and decodes the mixed batch.  Requests: a backlog of
-    4 x batch requests whose prompt lengths follow the workload's length law
-    and which generate 32..256 tokens each (uniform), all arrived at step 0,
-    at most `batch` running.  K steps are timed after W warm-up steps."""
-    import ctypes
-
+    """The serving loop over one layer's pools, one native call per step
+    (pkv_serve_step): the scheduler step (retire, admit, one token per
+    running sequence), the staging of its slots, context lengths and block
+    tables, the admitted prompts' and the new tokens' K/V appends, and the
+    decode of the mixed batch.  Requests: a backlog of 4 x batch requests
+    whose prompt lengths follow the workload's length law and which generate
+    32..256 tokens each (uniform), all arrived at step 0, at most `batch`
+    running.  K steps are timed after W warm-up steps: once as issued (the
+    host runs ahead of the GPU), once with HIP events around each step's
+    device work, which give the GPU's busy time per step and the gaps between
+    steps."""
     import numpy as np
     import torch
 
@@ -441,160 +443,52 @@ def bench_serve(args) -> None:
         scales = [None, None]
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
-    rows_prompt = [torch.randn((int(prompts.max()), Hkv, D), generator=gen, device=dev).to(torch_dtype(src_t))
+    # every admitted prompt's rows come from one buffer of the largest
+    # step's size (all B sequences admitted at once with the longest prompt)
+    max_prompt_tokens = B * int(prompts.max())
+    rows_prompt = [torch.randn((max_prompt_tokens, Hkv, D), generator=gen, device=dev).to(torch_dtype(src_t))
                    for _ in range(2)]
     rows_new = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch_dtype(src_t)) for _ in range(2)]
     q = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch_dtype(cfg.q_dtype))
-    out = torch.empty_like(q)
-    bt_max = torch.zeros((B, max_blocks), dtype=torch.int32, device=dev)
-    ctx_max = torch.zeros(B, dtype=torch.int32, device=dev)
-    a = pkv.decode_args(q, pools[0], pools[1], bt_max, ctx_max, cfg.scale, max_context_len=cap,
-                        k_scale=scales[0], v_scale=scales[1], out=out)
-    ws = pkv.alloc_workspace(a, q.device)
-    ctr = pkv.alloc_merge_counters(a, q.device)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    e_kv = 1 if byte else 2
     pool = pkv.KVPool(cfg.num_pages, PS, initial_free_order=rng.permutation(cfg.num_pages))
     sch = pkv.Scheduler(pool, B, pkv.CONTINUOUS)
     for i in range(n_req):
         sch.submit(i, int(prompts[i]), int(new_tok[i]), 0)
-
-    # per-step host -> device staging: [new slots int64 | context lens | block
-    # tables], a ring of pinned host buffers, one copy per step; a buffer is
-    # reused once its copy has completed (polled, not waited on: a blocking
-    # event wait costs a wake-up of ~0.2 ms here)
-    from paged_kv_cache_266_amd._lib import DTYPE_CODES, WriteArgs, check, lib
-
-    L = lib()
-    # host -> device copies straight through the HIP runtime torch has loaded
-    # (torch's copy_ of a slice of pinned memory looks the pointer up first)
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipMemcpyAsync.restype = ctypes.c_int
-    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
-    H2D = 1
-
-    def h2d(dst_ptr, src_ptr, nbytes):
-        if hip.hipMemcpyAsync(dst_ptr, src_ptr, nbytes, H2D, sh) != 0:
-            raise RuntimeError("hipMemcpyAsync failed")
-
-    words = 3 * B + B * max_blocks
-    RING = 16
-    pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(RING)]
-    pin_np = [t.numpy() for t in pin]
-    copied = [None] * RING
-    stage = torch.empty(words, dtype=torch.int32, device=dev)
-    slots_dev = stage[:2 * B].view(torch.int64)
-    wa = WriteArgs()
-    wa.k_new, wa.v_new = rows_new[0].data_ptr(), rows_new[1].data_ptr()
-    wa.slots = slots_dev.data_ptr()
-    wa.k_pool, wa.v_pool = pools[0].data_ptr(), pools[1].data_ptr()
-    wa.k_scale = 0 if scales[0] is None else scales[0].data_ptr()
-    wa.v_scale = 0 if scales[1] is None else scales[1].data_ptr()
-    wa.num_kv_heads, wa.head_dim, wa.page_size, wa.num_pages = Hkv, D, PS, cfg.num_pages
-    wa.kv_dtype, wa.src_dtype = DTYPE_CODES[cfg.kv_dtype], DTYPE_CODES[src_t]
-    a.workspace = 0 if ws is None else ws.data_ptr()
-    a.workspace_bytes = 0 if ws is None else ws.numel()
-    a.merge_counters = 0 if ctr is None else ctr.data_ptr()
-    a.merge_counter_bytes = 0 if ctr is None else 4 * ctr.numel()
-    a.context_lens = stage[2 * B:].data_ptr()
-    a.block_tables = stage[3 * B:].data_ptr()
-    # admitted prompts' slots: pinned host buffers in turn, one copy each
-    max_prompt_slots = B * int(prompts.max())
-    ppin = [torch.empty(max_prompt_slots, dtype=torch.int64, pin_memory=True) for _ in range(RING)]
-    ppin_np = [t.numpy() for t in ppin]
-    pcopied = [None] * RING
-    pstage = torch.empty(max_prompt_slots, dtype=torch.int64, device=dev)
-    host_s = [0.0]
-    parts = {"sched_step": 0.0, "prompts": 0.0, "poll": 0.0, "tables": 0.0, "launch": 0.0}
-    evs = []
-    k = [0]
-
-    def one_step(timed_events):
-        t_h = time.perf_counter()
-        s = sch.step()
-        t_1 = time.perf_counter()
-        parts["sched_step"] += t_1 - t_h
-        if len(s.admitted):
-            i = k[0] % RING
-            while pcopied[i] is not None and not pcopied[i].query():
-                time.sleep(2e-5)
-            off, spans = 0, []
-            for sid in s.admitted:
-                pages = np.asarray(pool.pages(int(sid)), dtype=np.int64)
-                n = int(prompts[int(sid)])
-                t = np.arange(n, dtype=np.int64)
-                ppin_np[i][off:off + n] = pages[t // PS] * PS + t % PS
-                spans.append((off, n))
-                off += n
-            h2d(pstage.data_ptr(), ppin[i].data_ptr(), off * 8)
-            pcopied[i] = torch.cuda.Event()
-            pcopied[i].record(stream)
-            for off, n in spans:
-                pkv.write_kv(rows_prompt[0][:n], rows_prompt[1][:n], pstage[off:off + n], pools[0], pools[1],
-                             k_scale=scales[0], v_scale=scales[1])
-        t_2 = time.perf_counter()
-        parts["prompts"] += t_2 - t_1
-        n = len(s.seq_ids)
-        if n == 0:
-            host_s[0] += time.perf_counter() - t_h
-            return 0, 0
-        i = k[0] % RING
-        k[0] += 1
-        while copied[i] is not None and not copied[i].query():
-            time.sleep(2e-5)                 # the copy from this buffer RING steps ago
-        t_p = time.perf_counter()
-        parts["poll"] += t_p - t_2
-        t_2 = t_p
-        h = pin_np[i]
-        h[:2 * B].view(np.int64)[:n] = s.new_slots
-        bt, ctx = sch.batch_tables(max_blocks, h[3 * B:3 * B + n * max_blocks].reshape(n, max_blocks),
-                                   h[2 * B:2 * B + n])
-        t_3 = time.perf_counter()
-        parts["tables"] += t_3 - t_2
-        if timed_events is not None:
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            ev[0].record(stream)
-        h2d(stage.data_ptr(), pin[i].data_ptr(), words * 4)
-        copied[i] = torch.cuda.Event()
-        copied[i].record(stream)
-        if timed_events is not None:
-            ev[1].record(stream)
-        wa.n = n
-        check(L.pkv_write_kv(ctypes.byref(wa), sh), "write_kv")
-        a.batch, a.max_blocks = n, max_blocks
-        t_4 = time.perf_counter()
-        parts["launch"] += t_4 - t_3
-        host_s[0] += t_4 - t_h
-        if timed_events is not None:
-            ev[2].record(stream)
-        check(L.pkv_paged_attn_decode(ctypes.byref(a), sh), "decode")
-        if timed_events is not None:
-            ev[3].record(stream)
-            timed_events.append(ev)
-        kv = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * e_kv + (int(ctx.sum()) * Hkv * 8 if byte else 0)
-        return n, kv
-
+    stream = torch.cuda.current_stream()
+    loop = pkv.ServeLoop(sch, q, pools[0], pools[1], cfg.scale, k_new=rows_new[0], v_new=rows_new[1],
+                         k_prompt=rows_prompt[0], v_prompt=rows_prompt[1], max_blocks=max_blocks,
+                         k_scale=scales[0], v_scale=scales[1], ring=8, stream=stream)
+    e_kv = 1 if byte else 2
     for _ in range(args.warmup):
-        one_step(None)
+        loop.step()
     torch.cuda.synchronize()
-    host_s[0] = 0.0
-    for key in parts:
-        parts[key] = 0.0
+
+    # pass 1: as issued
+    tokens = 0
     t0 = time.perf_counter()
-    tokens = kv_bytes = 0
+    host = wait = 0.0
     for _ in range(args.steps):
-        n, kv = one_step(evs)
-        tokens += n
-        kv_bytes += kv
+        h0 = time.perf_counter()
+        r = loop.step()
+        host += time.perf_counter() - h0
+        wait += r.slot_wait_us * 1e-6
+        tokens += r.sched.n_running
+    t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    dec_ms = float(sum(e[2].elapsed_time(e[3]) for e in evs))
-    gpu_parts = {"copy": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
-                 "write_kv": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
-                 "decode": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3,
-                 "between_steps": float(np.mean([a_[3].elapsed_time(b_[0]) for a_, b_ in zip(evs, evs[1:])])) * 1e3}
+    # pass 2: events around each step's device work
+    evs = []
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        r = loop.step()
+        ev[1].record(stream)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    busy = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    gaps = [a_[1].elapsed_time(b_[0]) * 1e3 for a_, b_ in zip(evs, evs[1:])]
     st_ = sch.stats()
+    loop.close()
     sch.close()
     pool.close()
     print(json.dumps({
@@ -603,13 +497,16 @@ def bench_serve(args) -> None:
         "warmup": args.warmup, "ms_per_step": round(el * 1e3 / args.steps, 4), "higher_is_better": True,
         "dtype": cfg.kv_dtype, "data": "synthetic",
         "config": {"workload": f"serve_{cfg.name}", "max_batch": B, "requests": n_req,
-                   "prompt_law": cfg.lens_kind, "new_tokens": "uniform 32..256", "page_size": PS},
+                   "prompt_law": cfg.lens_kind, "new_tokens": "uniform 32..256", "page_size": PS,
+                   "kv_bytes_per_token_per_layer": 2 * Hkv * D * e_kv},
         "avg_batch": round(tokens / args.steps, 2),
-        "decode_kernel_us_per_step": round(dec_ms * 1e3 / max(len(evs), 1), 2),
-        "decode_kv_GBps": round(kv_bytes / (dec_ms * 1e-3) / 1e9, 1) if dec_ms else None,
-        "host_us_per_step": round(host_s[0] * 1e6 / args.steps, 1),
-        "host_us_breakdown": {key: round(v * 1e6 / args.steps, 1) for key, v in parts.items()},
-        "gpu_us_breakdown": {key: round(v, 1) for key, v in gpu_parts.items()},
+        "host_us_per_step": round((host - wait) * 1e6 / args.steps, 1),
+        "host_slot_wait_us_per_step": round(wait * 1e6 / args.steps, 1),
+        "host_issue_us_per_step": round(t_issue * 1e6 / args.steps, 1),
+        "gpu_busy_us_per_step": round(busy, 2),
+        "gpu_idle_us_between_steps": {"mean": round(float(np.mean(gaps)), 2),
+                                      "median": round(float(np.median(gaps)), 2),
+                                      "p90": round(float(np.percentile(gaps, 90)), 2)},
         "scheduler": {"now": st_["now"], "finished": st_["finished"], "waiting": st_["waiting"]},
     }), flush=True)
 

@@ -520,6 +520,82 @@ typedef struct pkv_sched_stats {
 
 pkv_status pkv_sched_get_stats(const pkv_sched *sched, pkv_sched_stats *out);
 
+/* ===================================================================== *
+ * Host + device: one serving step per call over one layer's pools -- the
+ * three parts of a step of "TensorRT-LLM 深度实战", section 3.2 (retire
+ * finished sequences, admit waiting ones, one forward pass over the running
+ * batch) with the attention of that pass: the scheduler step (pkv_sched_step),
+ * the K/V of the admitted prompts' tokens and of every running sequence's new
+ * token written at their slots (pkv_write_kv), and the decode of the batch
+ * (pkv_paged_attn_decode).  The host work (scheduling, prompt slots, block
+ * tables) runs in native code and lands in one slot of a caller-provided ring
+ * of pinned host buffers, which one copy moves to device memory; the device
+ * work is enqueued on `stream` without waiting for it, so the host may run up
+ * to `ring` steps ahead of the GPU.  A slot is reused only after the copy
+ * that read it has completed.  Use one stream for all steps of an object.
+ * ===================================================================== */
+
+typedef struct pkv_serve pkv_serve;
+
+typedef struct pkv_serve_desc {
+    pkv_sched *sched;           /* the step driver (and through it the pool); must
+                                   outlive this object and be used by it alone      */
+    int32_t max_blocks;         /* block-table row length of the decode; every
+                                   sequence's pages must fit                        */
+    int32_t max_prompt_tokens;  /* bound on the prompt tokens admitted in one step  */
+    int32_t ring;               /* staging slots, >= 1                              */
+    void *host_staging;         /* host, PINNED (hipHostMalloc or equivalent),
+                                   ring x pkv_serve_slot_bytes bytes, 16-byte aligned */
+    void *dev_staging;          /* device, pkv_serve_slot_bytes bytes, 16-byte aligned */
+    pkv_decode_args decode;     /* template of each step's decode: q, pools,
+                                   scales, out, workspace and merge counters (sized
+                                   for batch = the scheduler's max_batch and
+                                   max_context_len = max_blocks x page_size), head
+                                   counts, head_dim, page_size, num_pages,
+                                   num_splits, dtypes, scale.  batch, block_tables,
+                                   context_lens, max_blocks and max_context_len are
+                                   set by each step.                                 */
+    pkv_write_args append;      /* template of each step's append of the new tokens:
+                                   k_new / v_new [max_batch][Hkv][D] rows in batch
+                                   order (and their scales for encoded rows), the
+                                   pools and their scales, num_kv_heads, head_dim,
+                                   page_size, num_pages, kv_dtype, src_dtype.  slots
+                                   and n are set by each step.                       */
+    const void *k_prompt;       /* device [max_prompt_tokens][Hkv][D], the append's
+                                   src_dtype: the admitted prompts' K/V rows, packed
+                                   prompt after prompt in admission order            */
+    const void *v_prompt;
+    const float *k_prompt_scale; /* their scales for encoded rows, else NULL        */
+    const float *v_prompt_scale;
+} pkv_serve_desc;
+
+typedef struct pkv_serve_step_out {
+    pkv_sched_step_out sched;   /* the scheduler step (clock, batch size, admitted,
+                                   retired)                                          */
+    int32_t prompt_tokens;      /* admitted prompts' tokens written this step       */
+    int32_t max_context_len;    /* longest context of the batch after the append    */
+    float slot_wait_us;         /* host time this call spent waiting for a staging
+                                   slot (the host was `ring` steps ahead)            */
+} pkv_serve_step_out;
+
+/* Bytes of one staging slot for this descriptor (host_staging holds ring of
+ * them, dev_staging one). */
+pkv_status pkv_serve_slot_bytes(const pkv_serve_desc *desc, size_t *bytes);
+
+/* Creates the step object (host memory and `ring` HIP events, owned until
+ * pkv_serve_destroy).  INVALID_ARG for a bad descriptor, or the decode
+ * template's own error for the largest step. */
+pkv_status pkv_serve_create(const pkv_serve_desc *desc, pkv_serve **out);
+void pkv_serve_destroy(pkv_serve *serve);
+
+/* Runs one step.  seq_ids (host, may be NULL) receives the batch, in the order
+ * of the rows of q, out and the new-token K/V; this step's admissions are its
+ * last out->sched.n_admitted entries.  With nothing to run, no device work is
+ * enqueued.  If the step's admitted prompts exceed max_prompt_tokens, or a
+ * sequence has more pages than max_blocks, the scheduler step has happened but
+ * nothing is enqueued (WORKSPACE / INVALID_ARG). */
+pkv_status pkv_serve_step(pkv_serve *serve, void *stream, pkv_serve_step_out *out, int64_t *seq_ids);
+
 #ifdef __cplusplus
 }
 #endif

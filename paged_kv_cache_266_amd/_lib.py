@@ -37,6 +37,7 @@ EXPORTED = [
     "pkv_paged_attn_decode_noalloc", "pkv_write_kv", "pkv_seq_fork", "pkv_append_tokens_cow", "pkv_page_owners", "pkv_copy_pages",
     "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_submit", "pkv_sched_finish", "pkv_sched_step",
     "pkv_sched_get_stats", "pkv_sched_batch_tables", "pkv_paged_prefill",
+    "pkv_serve_slot_bytes", "pkv_serve_create", "pkv_serve_destroy", "pkv_serve_step",
 ]
 
 # The host-only build (page pool, scheduler, status codes; no GPU entry
@@ -124,6 +125,21 @@ class SchedStats(ctypes.Structure):
                 ("finished", ctypes.c_int64), ("wait_sum", ctypes.c_int64)]
 
 
+class ServeDesc(ctypes.Structure):
+    _fields_ = [
+        ("sched", ctypes.c_void_p), ("max_blocks", ctypes.c_int32), ("max_prompt_tokens", ctypes.c_int32),
+        ("ring", ctypes.c_int32), ("host_staging", ctypes.c_void_p), ("dev_staging", ctypes.c_void_p),
+        ("decode", DecodeArgs), ("append", WriteArgs),
+        ("k_prompt", ctypes.c_void_p), ("v_prompt", ctypes.c_void_p),
+        ("k_prompt_scale", ctypes.c_void_p), ("v_prompt_scale", ctypes.c_void_p),
+    ]
+
+
+class ServeStepOut(ctypes.Structure):
+    _fields_ = [("sched", SchedStepOut), ("prompt_tokens", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("slot_wait_us", ctypes.c_float)]
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
@@ -204,6 +220,10 @@ def _signatures():
         "pkv_paged_prefill": (ci, [P(PrefillArgs), vp]),
         "pkv_sched_batch_tables": (ci, [vp, i32, i32, P(i32), P(i32), P(i32)]),
         "pkv_sched_get_stats": (ci, [vp, P(SchedStats)]),
+        "pkv_serve_slot_bytes": (ci, [P(ServeDesc), P(sz)]),
+        "pkv_serve_create": (ci, [P(ServeDesc), P(vp)]),
+        "pkv_serve_destroy": (None, [vp]),
+        "pkv_serve_step": (ci, [vp, vp, P(ServeStepOut), P(i64)]),
     }
     for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_partitions", "pkv_splitk_reduce",
                  "pkv_paged_attn_decode_noalloc"):

@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["decode.hip", "api.cpp", "errors.cpp", "pool.cpp", "sched.cpp", "prefill.hip", "prefill_api.cpp"]
+SOURCES = ["decode.hip", "api.cpp", "errors.cpp", "pool.cpp", "sched.cpp", "serve.cpp", "prefill.hip",
+           "prefill_api.cpp"]
 # the host-only part (page pool, scheduler, status codes): plain C++, no HIP
 HOST_SOURCES = ["errors.cpp", "pool.cpp", "sched.cpp"]
 

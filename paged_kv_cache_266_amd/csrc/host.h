@@ -20,4 +20,8 @@ pkv_status fail(pkv_status code, const char *msg);
 int32_t pool_page_size(const pkv_pool *pool);
 int32_t pool_num_pages(const pkv_pool *pool);
 
+// The scheduler's pool and batch limit, for the serving step.
+pkv_pool *sched_pool(const pkv_sched *sched);
+int32_t sched_max_batch(const pkv_sched *sched);
+
 }  // namespace pkv

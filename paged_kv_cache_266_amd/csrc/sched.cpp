@@ -49,6 +49,9 @@ struct pkv_sched {
 
 using pkv::fail;
 
+pkv_pool *pkv::sched_pool(const pkv_sched *s) { return s->pool; }
+int32_t pkv::sched_max_batch(const pkv_sched *s) { return s->max_batch; }
+
 static int32_t held_pages(const pkv_sched *s, int64_t id)
 {
     int32_t pages = 0;

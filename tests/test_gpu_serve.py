@@ -168,3 +168,117 @@ def _quiet(case, out):
 
     err = np.abs(to_f64(out) - oracle.paged_decode(case)).max()
     assert err <= TOL[case.cfg.kv_dtype], f"max |gpu - oracle| = {err}"
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,qd,kvd,PS,max_batch,ring", [
+    (32, 8, 128, "bf16", "bf16", 16, 4, 3),
+    (16, 16, 128, "f16", "i8", 16, 5, 2),
+    (8, 2, 64, "bf16", "fp8", 64, 3, 1),
+])
+def test_native_serve_step_matches_oracle(Hq, Hkv, D, qd, kvd, PS, max_batch, ring):
+    """pkv_serve_step: one library call per step schedules, stages, appends
+    the admitted prompts' and new tokens' K/V and decodes.  First each step
+    is synchronised and its output compared with the oracle over a host
+    mirror of the pools; then the remaining steps run back to back (the host
+    ahead of the GPU by up to `ring` staging slots) and the final pools are
+    compared byte for byte with the mirror, the last step's output with the
+    oracle."""
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+
+    note(f"native serve: Hq {Hq} Hkv {Hkv} D {D} {qd}/{kvd} PS {PS} max_batch {max_batch} ring {ring}")
+    rng = np.random.default_rng(77)
+    n_req, max_prompt, max_new = 14, 120, 10
+    cap = max_prompt + max_new
+    max_blocks = -(-cap // PS)
+    num_pages = max_batch * max_blocks + 3
+    byte = kvd in ("i8", "fp8")
+    src = qd if byte else kvd
+    dev = "cuda"
+    shape = (num_pages, Hkv, PS, D)
+    if byte:
+        pools = [torch.zeros(shape, dtype=torch.uint8, device=dev).view(torch_dtype(kvd)) for _ in range(2)]
+        scales = [torch.zeros(shape[:3], dtype=torch.float32, device=dev) for _ in range(2)]
+        host = [np.zeros(shape, dtype=np.int8 if kvd == "i8" else np.uint8) for _ in range(2)]
+        host_s = [np.zeros(shape[:3], dtype=np.float32) for _ in range(2)]
+    else:
+        pools = [torch.zeros(shape, dtype=torch_dtype(kvd), device=dev) for _ in range(2)]
+        scales = [None, None]
+        host = [np.zeros(shape, dtype=np.uint16) for _ in range(2)]
+        host_s = [None, None]
+    max_prompt_tokens = max_batch * max_prompt
+    new_bits = [_to_bits(rng.standard_normal((max_batch, Hkv, D)).astype(np.float32), src) for _ in range(2)]
+    prompt_bits = [_to_bits(rng.standard_normal((max_prompt_tokens, Hkv, D)).astype(np.float32), src)
+                   for _ in range(2)]
+    q_bits = _to_bits(rng.standard_normal((max_batch, Hq, D)).astype(np.float32), qd)
+    cfg = small_config(Hq, Hkv, D, qd, kvd, PS, (cap,) * max_batch, num_pages=num_pages)
+
+    def mirror(rows_bits, slots):
+        if len(slots) == 0:
+            return
+        for w in range(2):
+            rows = rows_bits[w][:len(slots)]
+            if byte:
+                exact = (rows.view(np.float16).astype(np.float32) if src == "f16"
+                         else (rows.astype(np.uint32) << 16).view(np.float32))
+                codes, s = oracle.quantize_rows(exact, kvd)
+                oracle.scatter_rows(host[w], slots, codes)
+                oracle.scatter_rows(host_s[w][..., None], slots, s[..., None])
+            else:
+                oracle.scatter_rows(host[w], slots, rows)
+
+    def slots_of(pages, tokens):
+        return [pages[t // PS] * PS + t % PS for t in tokens]
+
+    with pkv.KVPool(num_pages, PS, initial_free_order=rng.permutation(num_pages)) as pool:
+        sch = pkv.Scheduler(pool, max_batch, pkv.CONTINUOUS)
+        arrive = 0
+        for i in range(n_req):
+            arrive += int(rng.integers(0, 3))
+            sch.submit(200 + i, int(rng.integers(0, max_prompt + 1)), int(rng.integers(1, max_new + 1)), arrive)
+        loop = pkv.ServeLoop(sch, _dev16(q_bits, qd, dev), pools[0], pools[1], cfg.scale,
+                             k_new=_dev16(new_bits[0], src, dev), v_new=_dev16(new_bits[1], src, dev),
+                             k_prompt=_dev16(prompt_bits[0], src, dev), v_prompt=_dev16(prompt_bits[1], src, dev),
+                             max_blocks=max_blocks, k_scale=scales[0], v_scale=scales[1], ring=ring)
+        steps = checked = 0
+        last = None
+        while not sch.done():
+            r = loop.step()
+            steps += 1
+            n = r.sched.n_running
+            if n == 0:
+                continue
+            ids = [int(x) for x in loop.seq_ids[:n]]
+            bt, ctx = pool.block_tables(ids, max_blocks)
+            assert int(ctx.max()) == r.max_context_len
+            # the mirror: admitted prompts (packed in admission order), then the new tokens
+            pslots = []
+            for i in range(n - r.sched.n_admitted, n):
+                pages = pool.pages(ids[i])
+                pslots += slots_of(pages, range(int(ctx[i]) - 1))
+            assert len(pslots) == r.prompt_tokens
+            mirror(prompt_bits, pslots)
+            mirror(new_bits, [slots_of(pool.pages(ids[i]), [int(ctx[i]) - 1])[0] for i in range(n)])
+            step_cfg = small_config(Hq, Hkv, D, qd, kvd, PS, (cap,) * n, num_pages=num_pages)
+            case = Case(cfg=step_cfg, seed=0, context_lens=ctx, free_order=np.arange(num_pages, dtype=np.int32),
+                        block_tables=bt, q_bits=q_bits[:n], used_pages=np.arange(num_pages, dtype=np.int32),
+                        page_index=np.arange(num_pages, dtype=np.int32), k_pages=host[0].copy(),
+                        v_pages=host[1].copy(), k_scale=None if host_s[0] is None else host_s[0].copy(),
+                        v_scale=None if host_s[1] is None else host_s[1].copy(), scale=cfg.scale)
+            if steps <= 12:
+                torch.cuda.synchronize()
+                compare(case, loop.out[:n], f"step {r.sched.step} batch {n}")
+                checked += 1
+            last = (case, n)
+        torch.cuda.synchronize()
+        compare(last[0], loop.out[:last[1]], "last step")
+        loop.close()
+        assert sch.stats()["finished"] == n_req and pool.free_page_count() == num_pages
+        sch.close()
+    for w in range(2):
+        got = pools[w].view(torch.uint8 if byte else torch.int16).cpu().numpy()
+        assert np.array_equal(got.view(host[w].dtype), host[w])
+        if byte:
+            assert np.array_equal(scales[w].cpu().numpy().view(np.uint32), host_s[w].view(np.uint32))
+    note(f"  {steps} steps, {checked} checked one by one, the rest back to back")
