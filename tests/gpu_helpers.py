@@ -9,11 +9,13 @@ import oracle
 from synth import get_config, make_case
 from synth.device import upload
 
-# max-abs tolerances on outputs, by KV storage type.  fp8 has no stated
-# tolerance: its codes decode exactly (as int8 codes do), the arithmetic is
-# the int8 path's fp32 accumulation, and the output rounding is the q type's,
-# so the bf16 bound is used.
-TOL = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 1.6e-2}
+# max-abs tolerances on outputs, by KV storage type.  fp8 E4M3 has no stated
+# tolerance; as the other 8-bit KV format with per-token scales it takes the
+# int8 bound.  Its codes decode exactly, but the matrix-core kernel rounds
+# each probability times its token's V scale to bf16 before the product, a
+# relative error of up to 2^-9 beside the output's own rounding: a
+# single-token output of magnitude 4.7 can be off by 1.8e-2.
+TOL = {"f16": 4e-3, "bf16": 1.6e-2, "i8": 2.5e-2, "fp8": 2.5e-2}
 
 
 def note(msg):
