@@ -310,6 +310,28 @@ __device__ __forceinline__ void store_coherent1(float *base, int bytes, int voff
                                           0, kCoherent);
 }
 
+// ---- the first piece of a wave's range ----------------------------------------
+//
+// A wave's range can start inside a segment that began in an earlier wave's
+// range; that segment ends inside the range, and its piece is the only one a
+// wave finishes before the end of its range.  Pieces are written with
+// system-coherent stores, which complete only once they have reached memory,
+// and vector memory operations complete in issue order: a coherent store in
+// the middle of the stream would hold up every later wait for the next
+// tiles' loads.  So the first piece is kept in LDS and written after the
+// wave's last tile, where the merge waits for the stores anyway.
+
+template <int D, int G>
+__device__ __forceinline__ void flush_first_piece(const DecodeParams &p, int slot, const float *so,
+                                                  const float2 *sml, int lane)
+{
+    float *po = uniform_fptr(p.part_o + (size_t)slot * G * D);
+    for (int i = lane; i < G * D / 4; i += 64)
+        store_coherent4(po, G * D * 4, i * 16, reinterpret_cast<const float4 *>(so)[i]);
+    if (lane < G)
+        store_coherent2(uniform_fptr(p.part_ml + (size_t)slot * G * 2), G * 8, lane * 8, sml[lane]);
+}
+
 // ---- the partition kernel ---------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -841,6 +863,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // records (segment, first wave, wave count) wait in LDS, not registers.
     __shared__ int s_pend[2][3];
     __shared__ int s_npend;
+    __shared__ __align__(16) float s_first[G * D];   // the range's first piece, written after the last tile
+    __shared__ float2 s_first_ml[G];
+    int first_slot = -1;
     if (lane == 0)
         s_npend = 0;
 
@@ -1033,6 +1058,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                         for (int v = 0; v < EPL / 8; ++v)
                             o[v] = u32x4{packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]};
+                    } else if (!piece_from_start && !last_in_range) {
+                        // the range's first piece: to LDS, written after the last tile
+#pragma unroll
+                        for (int v = 0; v < EPL / 4; ++v)
+                            *reinterpret_cast<float4 *>(s_first + h * D + EPL * j + 4 * v) =
+                                any_bad ? make_float4(nan, nan, nan, nan)
+                                        : make_float4(acc[h][4 * v], acc[h][4 * v + 1], acc[h][4 * v + 2],
+                                                      acc[h][4 * v + 3]);
+                        if (j == 0)
+                            s_first_ml[h] = make_float2(m_run[h], any_bad ? nan : lt);
                     } else {
                         // piece group of slot (seg + w): G heads x D values, G (m, l) pairs
                         const size_t slot = (size_t)seg + (size_t)w;
@@ -1049,6 +1084,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     }
                 }
             }
+            if (!whole && !piece_from_start && !last_in_range)
+                first_slot = seg + (int)w;
             if (!whole) {
                 const long long first = t - cur.k;   // the segment's first global tile
                 const int w0 = (int)owner_of(first, T, NWe);
@@ -1087,10 +1124,12 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         cur = nxt;
     }
 
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (first_slot >= 0)
+        flush_first_piece<D, G>(p, first_slot, s_first, s_first_ml, lane);
     if (p.fused) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int npend = __builtin_amdgcn_readfirstlane(s_npend);
         for (int i = 0; i < npend; ++i)
             settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),
@@ -1222,6 +1261,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     __shared__ float s_p[16 * 64];   // probabilities times V scales: [head][token % 4][token / 4]
     __shared__ int s_pend[2][3];
     __shared__ int s_npend;
+    __shared__ __align__(16) float s_first[G * D];   // the range's first piece, written after the last tile
+    __shared__ float2 s_first_ml[G];
+    int first_slot = -1;
 
     const int lane = threadIdx.x;
     const int a = lane / 16, c = lane % 16;
@@ -1533,6 +1575,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
                                          pack_out<QT>(acc[6][v] * inv, acc[7][v] * inv)};
                         *reinterpret_cast<u32x4 *>(reinterpret_cast<u32 *>(p.out) + (unit * D + 8 * (4 * a + v)) / 2) = o;
                     }
+                } else if (!piece_from_start && !last_in_range) {
+                    // the range's first piece: to LDS, written after the last tile
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float *dst = s_first + c * D + 8 * (4 * a + v);
+                        *reinterpret_cast<float4 *>(dst) =
+                            any_bad ? make_float4(nan, nan, nan, nan)
+                                    : make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
+                        *reinterpret_cast<float4 *>(dst + 4) =
+                            any_bad ? make_float4(nan, nan, nan, nan)
+                                    : make_float4(acc[4][v], acc[5][v], acc[6][v], acc[7][v]);
+                    }
+                    if (a == 0)
+                        s_first_ml[c] = make_float2(m_c, any_bad ? nan : l_c);
                 } else {
                     const size_t slot = (size_t)seg + (size_t)w;
                     float *po = uniform_fptr(p.part_o + slot * G * D);
@@ -1551,6 +1607,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
                                         make_float2(m_c, any_bad ? nan : l_c));
                 }
             }
+            if (!whole && !piece_from_start && !last_in_range)
+                first_slot = seg + (int)w;
             if (!whole) {
                 const long long first = t - cur.k;
                 const int w0 = (int)owner_of(first, T, NWe);
@@ -1586,10 +1644,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
         nxt = nx2;
     }
 
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (first_slot >= 0)
+        flush_first_piece<D, G>(p, first_slot, s_first, s_first_ml, lane);
     if (p.fused) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int npend = __builtin_amdgcn_readfirstlane(s_npend);
         for (int i = 0; i < npend; ++i)
             settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),

@@ -234,3 +234,48 @@ def test_merge_soak_200_calls_bitwise():
     torch.cuda.synchronize()
     assert bool(same)
     assert int(ctr.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# fp8 at head_dim 128 (the matrix-core kernel) at several wave counts, with
+# segments shared by many waves (pieces kept in LDS until a wave's last tile,
+# then merged in the launch): 30 calls in a row are bitwise equal to the
+# first, the first matches the oracle, and the merge counters are zero after
+# the calls.
+
+@pytest.mark.parametrize("PS,G,splits", [(64, 4, 0), (64, 4, 7), (16, 4, 300), (64, 8, 64), (16, 1, 1),
+                                         (64, 2, 2000)])
+def test_fp8_repeated_calls_bitwise_and_counters_zero(PS, G, splits):
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    lens = (3000, 1, 64, 65, 9000, 128, 700, 4096, 0, 2500)
+    cfg = small_config(2 * G, 2, 128, "bf16", "fp8", PS, lens)
+    case = make_case(cfg, seed=95 + G + PS)
+    dev = upload(case, "cuda")
+    out = torch.empty_like(dev.q)
+    a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                        max_context_len=cfg.max_context_len, out=out, k_scale=dev.k_scale, v_scale=dev.v_scale,
+                        num_splits=splits)
+    ws = pkv.alloc_workspace(a, "cuda")
+    ctr = pkv.alloc_merge_counters(a, "cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    a.merge_counters, a.merge_counter_bytes = ctr.data_ptr(), 4 * ctr.numel()
+    sh = torch.cuda.current_stream().cuda_stream
+    note(f"[fp8 repeated calls] PS={PS} G={G} splits={splits} waves={lib().pkv_decode_num_splits(ctypes.byref(a))}")
+    check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+    torch.cuda.synchronize()
+    first = out.clone()
+    compare(case, first, "first call")
+    assert int(ctr.abs().sum()) == 0
+    same = torch.ones((), dtype=torch.bool, device="cuda")
+    for _ in range(29):
+        check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+        same &= (out.view(torch.int16) == first.view(torch.int16)).all()
+    torch.cuda.synchronize()
+    assert bool(same)
+    assert int(ctr.abs().sum()) == 0
