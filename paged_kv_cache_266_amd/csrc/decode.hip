@@ -310,28 +310,6 @@ __device__ __forceinline__ void store_coherent1(float *base, int bytes, int voff
                                           0, kCoherent);
 }
 
-// ---- the first piece of a wave's range ----------------------------------------
-//
-// A wave's range can start inside a segment that began in an earlier wave's
-// range; that segment ends inside the range, and its piece is the only one a
-// wave finishes before the end of its range.  Pieces are written with
-// system-coherent stores, which complete only once they have reached memory,
-// and vector memory operations complete in issue order: a coherent store in
-// the middle of the stream would hold up every later wait for the next
-// tiles' loads.  So the first piece is kept in LDS and written after the
-// wave's last tile, where the merge waits for the stores anyway.
-
-template <int D, int G>
-__device__ __forceinline__ void flush_first_piece(const DecodeParams &p, int slot, const float *so,
-                                                  const float2 *sml, int lane)
-{
-    float *po = uniform_fptr(p.part_o + (size_t)slot * G * D);
-    for (int i = lane; i < G * D / 4; i += 64)
-        store_coherent4(po, G * D * 4, i * 16, reinterpret_cast<const float4 *>(so)[i]);
-    if (lane < G)
-        store_coherent2(uniform_fptr(p.part_ml + (size_t)slot * G * 2), G * 8, lane * 8, sml[lane]);
-}
-
 // ---- the partition kernel ---------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -542,8 +520,12 @@ __device__ __forceinline__ void locate(const DecodeParams &p, const Lens &lens, 
 // atomic), and the merging wave reads only after its own count returned.
 
 template <int D, int G, int QT>
-__device__ __forceinline__ void settle_piece(const DecodeParams &p, int seg, int w0, int n, int w, int lane)
+__device__ __forceinline__ void settle_piece(const DecodeParams &p, int seg, int w0, int n, int w, int lane,
+                                             bool arrived0 = false)
 {
+    // arrived0: the piece's arrival at level 0 has been counted already (by
+    // settle_pending, for all of a wave's pieces at once) and completed its
+    // block
     constexpr int LPH = 64 / G;     // lanes per query head
     constexpr int DPL = D / LPH;    // output dims per lane
     constexpr int FAN = 8;
@@ -556,17 +538,19 @@ __device__ __forceinline__ void settle_piece(const DecodeParams &p, int seg, int
         const int parent = k - k % (span * FAN);
         const int children = min(FAN, (n - parent + span - 1) / span);
         if (children > 1) {
-            // this wave's stores (the piece, or the block it merged) complete
-            // before its arrival is counted
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_s_waitcnt(0);
-            uint32_t old = 0;
-            if (lane == 0)
-                old = __builtin_amdgcn_atomic_inc32(p.counters + level * level_stride + slot0 + parent,
-                                                    (uint32_t)(children - 1), __ATOMIC_RELAXED, "");
-            old = __builtin_amdgcn_readfirstlane(old);
-            if (old != (uint32_t)(children - 1))
-                return;               // a later arrival completes this block
+            if (!(arrived0 && level == 0)) {
+                // this wave's stores (the piece, or the block it merged)
+                // complete before its arrival is counted
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_s_waitcnt(0);
+                uint32_t old = 0;
+                if (lane == 0)
+                    old = __builtin_amdgcn_atomic_inc32(p.counters + level * level_stride + slot0 + parent,
+                                                        (uint32_t)(children - 1), __ATOMIC_RELAXED, "");
+                old = __builtin_amdgcn_readfirstlane(old);
+                if (old != (uint32_t)(children - 1))
+                    return;               // a later arrival completes this block
+            }
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
             float mc[FAN], lc[FAN], oc[FAN][DPL];
@@ -646,6 +630,62 @@ __device__ __forceinline__ void settle_piece(const DecodeParams &p, int seg, int
                 store_coherent2(uniform_fptr(p.part_ml + slot * G * 2), G * 8, h * 8, make_float2(M, L));
         }
         k = parent;
+    }
+}
+
+// ---- the first piece of a wave's range ----------------------------------------
+//
+// A wave's range can start inside a segment that began in an earlier wave's
+// range; that segment ends inside the range, and its piece is the only one a
+// wave finishes before the end of its range.  Pieces are written with
+// system-coherent stores, which complete only once they have reached memory,
+// and vector memory operations complete in issue order: a coherent store in
+// the middle of the stream would hold up every later wait for the next
+// tiles' loads.  So the first piece is kept in LDS and written after the
+// wave's last tile, where the merge waits for the stores anyway.
+
+template <int D, int G>
+__device__ __forceinline__ void flush_first_piece(const DecodeParams &p, int slot, const float *so,
+                                                  const float2 *sml, int lane)
+{
+    float *po = uniform_fptr(p.part_o + (size_t)slot * G * D);
+    for (int i = lane; i < G * D / 4; i += 64)
+        store_coherent4(po, G * D * 4, i * 16, reinterpret_cast<const float4 *>(so)[i]);
+    if (lane < G)
+        store_coherent2(uniform_fptr(p.part_ml + (size_t)slot * G * 2), G * 8, lane * 8, sml[lane]);
+}
+
+// A wave's pieces waiting for the merge (at most two: the segments its range
+// starts and ends inside), once their stores have been issued: the level-0
+// arrivals of all of them at once (lane i for piece i), so that their round
+// trips overlap, then, one piece at a time, the merge of each block an
+// arrival completed and the climb above it.
+template <int D, int G, int QT>
+__device__ __forceinline__ void settle_pending(const DecodeParams &p, const int (*pend)[3], int npend, int w,
+                                               int lane)
+{
+    constexpr int FAN = 8;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0);   // the pieces' stores have completed
+    int mode = 0;                    // 1: arrived and completed its block, 2: arrived, 3: no level-0 arrival
+    if (lane < npend) {
+        const int seg = pend[lane][0], w0 = pend[lane][1], n = pend[lane][2];
+        const int k = w - w0, parent = k - k % FAN, children = min(FAN, n - parent);
+        if (children > 1) {
+            const size_t slot0 = (size_t)seg + (size_t)w0;
+            const uint32_t old =
+                __builtin_amdgcn_atomic_inc32(p.counters + slot0 + parent, (uint32_t)(children - 1), __ATOMIC_RELAXED, "");
+            mode = old == (uint32_t)(children - 1) ? 1 : 2;
+        } else {
+            mode = 3;
+        }
+    }
+    for (int i = 0; i < npend; ++i) {
+        const int m = __builtin_amdgcn_readlane(mode, i);
+        if (m != 2)
+            settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(pend[i][0]),
+                                   __builtin_amdgcn_readfirstlane(pend[i][1]),
+                                   __builtin_amdgcn_readfirstlane(pend[i][2]), w, lane, m == 1);
     }
 }
 
@@ -870,8 +910,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         s_npend = 0;
 
     for (long long t = lo; t < hi; ++t) {
-        // the wave holding a segment's first tile records which waves share it
-        if (cur.k == 0 && lane == 0)
+        // the wave holding a segment's first tile records which waves share
+        // it (read by the merge kernel of the two-launch form only)
+        if (!p.fused && cur.k == 0 && lane == 0)
             p.seg_geo[cur.b * Hkv + cur.g] =
                 make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
         const bool last_in_range = t + 1 == hi;
@@ -1129,13 +1170,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (first_slot >= 0)
         flush_first_piece<D, G>(p, first_slot, s_first, s_first_ml, lane);
-    if (p.fused) {
-        const int npend = __builtin_amdgcn_readfirstlane(s_npend);
-        for (int i = 0; i < npend; ++i)
-            settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),
-                                   __builtin_amdgcn_readfirstlane(s_pend[i][1]),
-                                   __builtin_amdgcn_readfirstlane(s_pend[i][2]), (int)w, lane);
-    }
+    if (p.fused)
+        settle_pending<D, G, QT>(p, s_pend, __builtin_amdgcn_readfirstlane(s_npend), (int)w, lane);
 }
 
 // ---- fp8 KV on the matrix cores (head_dim 128) ---------------------------------
@@ -1437,7 +1473,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
             ph_nxt[pg] = -1;
 
     for (long long t = lo; t < hi; ++t) {
-        if (cur.k == 0 && lane == 0)
+        if (!p.fused && cur.k == 0 && lane == 0)
             p.seg_geo[cur.b * Hkv + cur.g] =
                 make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
         const bool last_in_range = t + 1 == hi;
@@ -1649,13 +1685,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (first_slot >= 0)
         flush_first_piece<D, G>(p, first_slot, s_first, s_first_ml, lane);
-    if (p.fused) {
-        const int npend = __builtin_amdgcn_readfirstlane(s_npend);
-        for (int i = 0; i < npend; ++i)
-            settle_piece<D, G, QT>(p, __builtin_amdgcn_readfirstlane(s_pend[i][0]),
-                                   __builtin_amdgcn_readfirstlane(s_pend[i][1]),
-                                   __builtin_amdgcn_readfirstlane(s_pend[i][2]), (int)w, lane);
-    }
+    if (p.fused)
+        settle_pending<D, G, QT>(p, s_pend, __builtin_amdgcn_readfirstlane(s_npend), (int)w, lane);
 }
 
 // ---- the merge kernel --------------------------------------------------------
