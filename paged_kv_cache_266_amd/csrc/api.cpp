@@ -199,6 +199,7 @@ static DecodeParams make_params(const pkv_decode_args *a)
     p.max_blocks = a->max_blocks;
     p.max_context_len = a->max_context_len;
     p.num_splits = resolve_splits(a);
+    p.first_round = std::min<int32_t>(p.num_splits, 4 * device_cu_count());   // four SIMDs per compute unit
     p.tag = next_tag();
     p.fused = 0;
     p.counters = a->merge_counters;

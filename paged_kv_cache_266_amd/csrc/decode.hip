@@ -464,16 +464,29 @@ __device__ __forceinline__ int batch_tiles(const DecodeParams &p, const Lens &le
     return total;
 }
 
-// Range of global tiles owned by wave w of NW.
-__device__ __forceinline__ long long range_start(long long w, long long T, long long NW)
+// Shares of the tile list.  With two waves on a SIMD, the one dispatched
+// first (wave w < H, H the waves that are first on their SIMD) wins the
+// issue arbitration and streams faster -- a third faster, measured with
+// per-wave timestamps on the fp8 kernel -- so those waves take WA shares of
+// the list and the others WB; with one wave per SIMD (H = NW) every wave
+// takes the same share.  Every share is non-empty when T >= 2 NW and
+// WA <= 2 WB (the kernels use H = NW otherwise).
+
+// First global tile of wave w's range.
+template <int WA, int WB>
+__device__ __forceinline__ long long range_start(long long w, long long T, long long NW, long long H)
 {
-    return w * T / NW;
+    static_assert(WB <= WA && WA <= 2 * WB, "share weights");
+    const long long ws = w < H ? WA * w : WA * H + WB * (w - H);
+    return ws * T / (WA * H + WB * (NW - H));
 }
 
 // The wave that owns global tile t (largest w with range_start(w) <= t).
-__device__ __forceinline__ long long owner_of(long long t, long long T, long long NW)
+template <int WA, int WB>
+__device__ __forceinline__ long long owner_of(long long t, long long T, long long NW, long long H)
 {
-    return ((t + 1) * NW - 1) / T;
+    const long long x = ((t + 1) * (WA * H + WB * (NW - H)) - 1) / T;   // largest share start <= t
+    return x < WA * H ? x / WA : min(NW - 1, H + (x - WA * H) / WB);
 }
 
 // Sequence containing global tile t (t < total) and the first global tile of
@@ -728,7 +741,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     const long long NWe = NW < T ? NW : T;
     if (w >= NWe)
         return;
-    const long long lo = range_start(w, T, NWe), hi = range_start(w + 1, T, NWe);
+    const long long H = p.first_round < NWe && T >= 2 * NWe ? p.first_round : NWe;
+    const long long lo = range_start<kShareA, kShareB>(w, T, NWe, H);
+    const long long hi = range_start<kShareA, kShareB>(w + 1, T, NWe, H);
     if (w == 0 && lane == 0)
         *p.ws_tag = p.tag;               // the merge kernel reads which call it follows
 
@@ -914,7 +929,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         // it (read by the merge kernel of the two-launch form only)
         if (!p.fused && cur.k == 0 && lane == 0)
             p.seg_geo[cur.b * Hkv + cur.g] =
-                make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
+                make_int4((int)p.tag, (int)w, (int)owner_of<kShareA, kShareB>(t + cur.nt - 1, T, NWe, H), 0);
         const bool last_in_range = t + 1 == hi;
         const Cursor nxt = last_in_range ? cur : advance(cur);
         const bool seg_end = last_in_range || nxt.k == 0;
@@ -1129,8 +1144,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 first_slot = seg + (int)w;
             if (!whole) {
                 const long long first = t - cur.k;   // the segment's first global tile
-                const int w0 = (int)owner_of(first, T, NWe);
-                const int w1 = (int)owner_of(first + cur.nt - 1, T, NWe);
+                const int w0 = (int)owner_of<kShareA, kShareB>(first, T, NWe, H);
+                const int w1 = (int)owner_of<kShareA, kShareB>(first + cur.nt - 1, T, NWe, H);
                 if (lane == 0) {
                     const int i = s_npend;
                     s_pend[i][0] = seg;
@@ -1321,7 +1336,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     const long long NWe = NW < T ? NW : T;
     if (w >= NWe)
         return;
-    const long long lo = range_start(w, T, NWe), hi = range_start(w + 1, T, NWe);
+    const long long H = p.first_round < NWe && T >= 2 * NWe ? p.first_round : NWe;
+    const long long lo = range_start<kShareFp8A, kShareFp8B>(w, T, NWe, H);
+    const long long hi = range_start<kShareFp8A, kShareFp8B>(w + 1, T, NWe, H);
     if (w == 0 && lane == 0)
         *p.ws_tag = p.tag;
 
@@ -1475,7 +1492,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     for (long long t = lo; t < hi; ++t) {
         if (!p.fused && cur.k == 0 && lane == 0)
             p.seg_geo[cur.b * Hkv + cur.g] =
-                make_int4((int)p.tag, (int)w, (int)owner_of(t + cur.nt - 1, T, NWe), 0);
+                make_int4((int)p.tag, (int)w, (int)owner_of<kShareFp8A, kShareFp8B>(t + cur.nt - 1, T, NWe, H), 0);
         const bool last_in_range = t + 1 == hi;
         const bool has_nx2 = t + 2 < hi;
         const Cursor nx2 = has_nx2 ? advance(nxt) : nxt;
@@ -1647,8 +1664,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
                 first_slot = seg + (int)w;
             if (!whole) {
                 const long long first = t - cur.k;
-                const int w0 = (int)owner_of(first, T, NWe);
-                const int w1 = (int)owner_of(first + cur.nt - 1, T, NWe);
+                const int w0 = (int)owner_of<kShareFp8A, kShareFp8B>(first, T, NWe, H);
+                const int w1 = (int)owner_of<kShareFp8A, kShareFp8B>(first + cur.nt - 1, T, NWe, H);
                 if (lane == 0) {
                     const int i = s_npend;
                     s_pend[i][0] = seg;

@@ -20,6 +20,18 @@ constexpr int kTileTokens = 64;
 // overlap with memory latency (fp8, Llama-3-8B shape: 67 vs 78 us).
 constexpr int kDefaultWavesPerCU = 4;
 constexpr int kDefaultWavesPerCUByte = 8;
+// Shares of the tile list taken by a wave dispatched first on its SIMD and
+// by one dispatched second (two waves per SIMD): vector kernel, fp8 kernel.
+#ifndef PKV_SHARE_A
+#define PKV_SHARE_A 4
+#define PKV_SHARE_B 3
+#endif
+#ifndef PKV_SHARE_FP8_A
+#define PKV_SHARE_FP8_A 4
+#define PKV_SHARE_FP8_B 3
+#endif
+constexpr int kShareA = PKV_SHARE_A, kShareB = PKV_SHARE_B;
+constexpr int kShareFp8A = PKV_SHARE_FP8_A, kShareFp8B = PKV_SHARE_FP8_B;
 
 enum DType : int { F16 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
 
@@ -45,6 +57,7 @@ struct DecodeParams {
     int32_t max_blocks;
     int32_t max_context_len;
     int32_t num_splits;   // waves of the persistent grid
+    int32_t first_round;  // waves dispatched first on their SIMD (one per SIMD)
     uint32_t tag;         // nonzero, different for every call
     int32_t fused;        // 1: the decode kernel merges shared segments itself
     float scale_log2;     // softmax scale * log2(e)
