@@ -705,7 +705,7 @@ __device__ __forceinline__ void settle_pending(const DecodeParams &p, const int 
 // ---- the partition kernel ---------------------------------------------------
 
 template <int D, int PS, int G, int QT, int KVT>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWavesPerGroup * 64) void paged_decode_kernel(DecodeParams p)
 {
     using S = Shape<D, PS, G, QT, KVT>;
     constexpr int R = S::R, TPI = S::TPI, EPL = S::EPL, PPT = S::PPT, LEVELS = S::LEVELS;
@@ -716,12 +716,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     using Chunk = typename S::Chunk;
     constexpr int CW = S::CB / 4;       // dwords per chunk
 
-    __shared__ float s_p[S::PSTRIDE];
+    // per-wave LDS: this wave's slot of the workgroup's arrays
+    const int slot = threadIdx.x / 64;
+    __shared__ float s_p_all[kWavesPerGroup][S::PSTRIDE];
+    float *const s_p = s_p_all[slot];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % 64;
     const int r = lane / R, j = lane % R;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
-    const long long NW = gridDim.x, w = blockIdx.x;
+    const long long NW = p.num_splits, w = (long long)blockIdx.x * kWavesPerGroup + slot;
+    if (w >= NW)
+        return;
 
     Lens lens;
     lens.load(p, lane);
@@ -916,10 +921,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // Pieces of shared segments this wave wrote (at most two: the segment its
     // range starts in and the one it ends in) are settled after the loop; the
     // records (segment, first wave, wave count) wait in LDS, not registers.
-    __shared__ int s_pend[2][3];
-    __shared__ int s_npend;
-    __shared__ __align__(16) float s_first[G * D];   // the range's first piece, written after the last tile
-    __shared__ float2 s_first_ml[G];
+    __shared__ int s_pend_all[kWavesPerGroup][2][3];
+    __shared__ int s_npend_all[kWavesPerGroup];
+    // the range's first piece, written after the last tile
+    __shared__ __align__(16) float s_first_all[kWavesPerGroup][G * D];
+    __shared__ float2 s_first_ml_all[kWavesPerGroup][G];
+    int (*const s_pend)[3] = s_pend_all[slot];
+    int &s_npend = s_npend_all[slot];
+    float *const s_first = s_first_all[slot];
+    float2 *const s_first_ml = s_first_ml_all[slot];
     int first_slot = -1;
     if (lane == 0)
         s_npend = 0;
@@ -1301,7 +1311,7 @@ struct Fp8KOperandTile {
 };
 
 template <int PS, int G, int QT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void paged_decode_fp8_mfma_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWavesPerGroup * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_decode_fp8_mfma_kernel(DecodeParams p)
 {
     constexpr int D = 128;
     using S = Shape<D, PS, G, QT, FP8>;
@@ -1309,17 +1319,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     static_assert(S::R == 16 && S::TPI == 4 && S::EPL == 8 && S::CB == 8, "layout of the 128-dim fp8 tile");
     static_assert(G <= 16, "one head per matrix row");
 
-    __shared__ float s_p[16 * 64];   // probabilities times V scales: [head][token % 4][token / 4]
-    __shared__ int s_pend[2][3];
-    __shared__ int s_npend;
-    __shared__ __align__(16) float s_first[G * D];   // the range's first piece, written after the last tile
-    __shared__ float2 s_first_ml[G];
+    // per-wave LDS: this wave's slot of the workgroup's arrays
+    const int slot = threadIdx.x / 64;
+    __shared__ float s_p_all[kWavesPerGroup][16 * 64];   // probabilities times V scales: [head][token % 4][token / 4]
+    __shared__ int s_pend_all[kWavesPerGroup][2][3];
+    __shared__ int s_npend_all[kWavesPerGroup];
+    // the range's first piece, written after the last tile
+    __shared__ __align__(16) float s_first_all[kWavesPerGroup][G * D];
+    __shared__ float2 s_first_ml_all[kWavesPerGroup][G];
+    float *const s_p = s_p_all[slot];
+    int (*const s_pend)[3] = s_pend_all[slot];
+    int &s_npend = s_npend_all[slot];
+    float *const s_first = s_first_all[slot];
+    float2 *const s_first_ml = s_first_ml_all[slot];
     int first_slot = -1;
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % 64;
     const int a = lane / 16, c = lane % 16;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
-    const long long NW = gridDim.x, w = blockIdx.x;
+    const long long NW = p.num_splits, w = (long long)blockIdx.x * kWavesPerGroup + slot;
+    if (w >= NW)
+        return;
 
     Lens lens;
     lens.load(p, lane);
@@ -2025,12 +2045,14 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(CopyParams p)
 template <int D, int PS, int G, int QT, int KVT>
 int launch_one(const DecodeParams &p, hipStream_t stream)
 {
-    dim3 grid((unsigned)p.num_splits);
+    // kWavesPerGroup independent waves per workgroup (fewer workgroups to
+    // dispatch); wave w is wave w % kWavesPerGroup of workgroup w / kWavesPerGroup
+    dim3 grid((unsigned)((p.num_splits + kWavesPerGroup - 1) / kWavesPerGroup));
     void *args[] = {const_cast<DecodeParams *>(&p)};
     const void *fn = (const void *)&paged_decode_kernel<D, PS, G, QT, KVT>;
     if constexpr (KVT == FP8 && D == 128)
         fn = (const void *)&paged_decode_fp8_mfma_kernel<PS, G, QT>;   // fp8 at head_dim 128: matrix cores
-    return (int)hipLaunchKernel(fn, grid, dim3(64), args, 0, stream);
+    return (int)hipLaunchKernel(fn, grid, dim3(kWavesPerGroup * 64), args, 0, stream);
 }
 
 template <int D, int PS, int G>

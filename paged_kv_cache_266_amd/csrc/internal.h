@@ -20,6 +20,10 @@ constexpr int kTileTokens = 64;
 // overlap with memory latency (fp8, Llama-3-8B shape: 67 vs 78 us).
 constexpr int kDefaultWavesPerCU = 4;
 constexpr int kDefaultWavesPerCUByte = 8;
+// Waves per workgroup of the decode kernels: independent waves (each streams
+// its own share), grouped only so that the dispatcher has a quarter as many
+// workgroups to place (measured: -1.5 us on the Llama-3-8B decode step).
+constexpr int kWavesPerGroup = 4;
 // Shares of the tile list taken by a wave dispatched first on its SIMD and
 // by one dispatched second (two waves per SIMD): vector kernel, fp8 kernel.
 #ifndef PKV_SHARE_A
