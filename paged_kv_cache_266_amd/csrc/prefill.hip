@@ -52,11 +52,11 @@
 //    q's type, V to f16, the type of the p.V product for these caches;
 //    the tile's per-token K and V scales go to LDS beside it, the K scale
 //    multiplies each score and the V scale each probability that weights V
-//    (the running sum takes the probabilities without it).  The V scales
-//    enter as vs * 2^-e, with 2^e above every V scale seen so far, so the
-//    f16 products stay in range and normal for any scale magnitude; O is
-//    rescaled by a power of two when e grows and multiplied by 2^e at the
-//    end.
+//    (the running sum takes the probabilities without it).  The
+//    exponentials carry 2^-e, with 2^e above every V scale seen so far, so
+//    the f16 products stay in range and normal for any scale magnitude; O
+//    and the sum carry the same factor (both rescaled by a power of two when
+//    e grows), which O / sum cancels.
 //
 // Key tiles after the block's last position are not visited.  A sequence
 // whose context length is invalid (negative, above the bound, shorter than
@@ -157,6 +157,15 @@ __device__ __forceinline__ int vt_column(int k)
     const int q = (k / 4) % 4;
     const int sq = q == 1 ? 2 : q == 2 ? 1 : q;
     return 16 * (k / 16) + 4 * sq + k % 4;
+}
+
+// Lane j of each 16-lane row reads lane (j + N) mod 16 of its row (DPP
+// row_ror; no LDS round trip).
+template <int N>
+__device__ __forceinline__ float row_ror(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + N, 0xF,
+                                                                 0xF, false));
 }
 
 template <int D, int PS, int G, int QT, int KVT>
@@ -350,11 +359,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (tid < 128)
                 s_sc[buf][tid / 64][tid % 64] = sv;
             if (wave == 1) {
-                // threads 64..127 (one wave) hold the tile's V scales
+                // threads 64..127 (one wave) hold the tile's V scales: the max
+                // over each 16-lane row by DPP rotations, then over the rows
                 float m = fabsf(sv);
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1)
-                    m = fmaxf(m, __shfl_xor(m, o));
+                m = fmaxf(m, row_ror<8>(m));
+                m = fmaxf(m, row_ror<4>(m));
+                m = fmaxf(m, row_ror<2>(m));
+                m = fmaxf(m, row_ror<1>(m));
+                auto at = [&](int l) {
+                    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), l));
+                };
+                m = fmaxf(fmaxf(at(0), at(16)), fmaxf(at(32), at(48)));
                 if (lane == 0)
                     s_vmax[buf] = m;
             }
@@ -393,12 +408,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float m_run = -3.0e38f, l_run = 0.0f;
     // Byte K/V: the probabilities that weight V are multiplied by the key's V
     // scale and rounded to f16 for the p.V product.  To keep that product in
-    // f16's normal range whatever the scales' magnitude, the V scales are
-    // applied as vs * 2^-e_run, with 2^e_run above every V scale seen so far
-    // (e_run only grows, tile by tile; O is rescaled by a power of two, an
-    // exact step, when it does), and the output is O * 2^e_run / sum.  The V
-    // scales of a tile are the same for every row, so e_run is uniform over
-    // the workgroup.  kNoExp: no nonzero V scale seen yet (O is zero).
+    // f16's normal range whatever the scales' magnitude, the exponentials
+    // carry 2^-e_run, with 2^e_run above every V scale seen so far (e_run only
+    // grows, tile by tile; O and the sum are rescaled by a power of two, an
+    // exact step, when it does), so O and the sum share the factor and O /
+    // sum is the output.  The V scales of a tile are the same for every row,
+    // so e_run is uniform over the workgroup.  kNoExp: no nonzero V scale
+    // seen yet (O is zero; the sum is kept in units of 2^0 until then).
     constexpr int kNoExp = -1000;
     int e_run = kNoExp;
 
@@ -501,41 +517,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int j = 0; j < 16; ++j)
                     oacc[db][j] *= alpha;
         }
+        // byte K/V: O and the sum are kept in units of 2^-e_run (e_run
+        // raised, never lowered, to the exponent bound of the largest V
+        // scale seen; O and the sum then scaled by the same power of two, an
+        // exact step), so the exponentials below carry 2^-e_run and O / sum
+        // needs no correction at the end
+        float m_eff = m_run;
+        if constexpr (kByte) {
+            const float vmax = s_vmax[BUF];
+            // 2^e_tile > vmax: the biased exponent of vmax minus 126
+            // (clamped to [-64, 64], which keeps the sum's terms, at most
+            // 2^(8 - e_run), inside fp32 for scales of any magnitude)
+            const int e_tile = vmax > 0.0f
+                                   ? min(max((int)((__builtin_bit_cast(u32, vmax) >> 23) & 0xFFu) - 126, -64), 64)
+                                   : kNoExp;
+            if (e_tile > e_run) {
+                const int d = (e_run == kNoExp ? 0 : e_run) - e_tile;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        oacc[db][j] = ldexpf(oacc[db][j], d);
+                l_run = ldexpf(l_run, d);
+                e_run = e_tile;
+            }
+            m_eff = m_run + (float)(e_run == kNoExp ? 0 : e_run);
+        }
         float ls = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 // a masked key (-inf) gives 0
-                const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][j], scale, -m_run));
+                const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][j], scale, -m_eff));
                 sc[kb][j] = e;
                 ls += e;
             }
         l_run += ls;
-        // byte K/V: the probabilities that weight V carry its V scale times
-        // 2^-e_run (the sum above takes neither)
+        // byte K/V: the probabilities that weight V carry its V scale (the
+        // sum above does not)
         if constexpr (kByte) {
-            const float vmax = s_vmax[BUF];
-            // 2^e_tile > vmax: the biased exponent of vmax minus 126
-            const int e_tile = vmax > 0.0f ? (int)((__builtin_bit_cast(u32, vmax) >> 23) & 0xFFu) - 126 : kNoExp;
-            if (e_tile > e_run) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        oacc[db][j] = ldexpf(oacc[db][j], max(e_run - e_tile, -300));
-                e_run = e_tile;
-            }
-            const float f = e_run == kNoExp ? 0.0f : ldexpf(1.0f, -e_run);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
                     const float4 vs = *reinterpret_cast<const float4 *>(&s_sc[BUF][1][32 * kb + 8 * j4 + 4 * h]);
-                    sc[kb][4 * j4] *= vs.x * f;
-                    sc[kb][4 * j4 + 1] *= vs.y * f;
-                    sc[kb][4 * j4 + 2] *= vs.z * f;
-                    sc[kb][4 * j4 + 3] *= vs.w * f;
+                    sc[kb][4 * j4] *= vs.x;
+                    sc[kb][4 * j4 + 1] *= vs.y;
+                    sc[kb][4 * j4 + 2] *= vs.z;
+                    sc[kb][4 * j4 + 3] *= vs.w;
                 }
         }
 
@@ -573,9 +603,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!valid_row)
         return;
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / l;
-    // byte K/V: O was accumulated in units of 2^e_run
-    const int e_out = kByte && e_run != kNoExp ? e_run : 0;
-    auto fin = [&](float x) { return kByte ? ldexpf(x * inv, e_out) : x * inv; };
+    auto fin = [&](float x) { return x * inv; };
     u32x2 *orow = reinterpret_cast<u32x2 *>((uint16_t *)p.out + ((size_t)(qs0 + tok) * Hq + head) * kD);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -279,3 +279,51 @@ def test_fp8_repeated_calls_bitwise_and_counters_zero(PS, G, splits):
     torch.cuda.synchronize()
     assert bool(same)
     assert int(ctr.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# More waves than SIMDs: the waves dispatched second on a SIMD take smaller
+# shares of the tile list than the first-round ones (when the list has at
+# least two tiles per wave).  Every kernel type on that path: outputs match
+# the oracle, repeat bitwise, and the merge counters return to zero.
+
+@pytest.mark.parametrize("qd,kvd,G", [("bf16", "bf16", 4), ("f16", "i8", 1), ("bf16", "fp8", 8), ("f16", "f16", 2)])
+def test_weighted_shares_more_waves_than_simds(qd, kvd, G):
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    props = torch.cuda.get_device_properties(0)
+    simds = 4 * props.multi_processor_count
+    splits = simds + simds // 2 + 7            # a second round of waves
+    Hkv = 8
+    per_seq = -(-2 * splits // Hkv)            # at least two tiles per wave in all
+    nseq = 6
+    lens = tuple(int(64 * (per_seq // nseq + 1) - 5 * i) for i in range(nseq))
+    cfg = small_config(G * Hkv, Hkv, 128, qd, kvd, 64, lens)
+    case = make_case(cfg, seed=123 + G)
+    dev = upload(case, "cuda")
+    out = torch.empty_like(dev.q)
+    a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                        max_context_len=cfg.max_context_len, out=out, k_scale=dev.k_scale, v_scale=dev.v_scale,
+                        num_splits=splits)
+    ws = pkv.alloc_workspace(a, "cuda")
+    ctr = pkv.alloc_merge_counters(a, "cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    a.merge_counters, a.merge_counter_bytes = ctr.data_ptr(), 4 * ctr.numel()
+    tiles = Hkv * sum(-(-n // 64) for n in lens)
+    note(f"[weighted shares] q={qd} kv={kvd} G={G} waves={splits} SIMDs={simds} tiles={tiles}")
+    assert tiles >= 2 * splits
+    sh = torch.cuda.current_stream().cuda_stream
+    check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+    torch.cuda.synchronize()
+    first = out.clone()
+    compare(case, first, "first call")
+    for _ in range(5):
+        check(lib().pkv_paged_attn_decode(ctypes.byref(a), sh))
+    torch.cuda.synchronize()
+    assert bool((out.view(torch.int16) == first.view(torch.int16)).all())
+    assert int(ctr.abs().sum()) == 0
