@@ -388,23 +388,36 @@ __device__ __forceinline__ int tiles_of(int n, int max_len)
     return n >= 0 && n <= max_len ? (n + kTileTokens - 1) / kTileTokens : 0;
 }
 
+// Integer sum and inclusive prefix sum over the 64 lanes, by DPP within each
+// 16-lane row and wave-uniform reads of the row totals (no LDS round trips:
+// both sit on the dependent chain before a wave's first load).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ int wave_sum_int(int x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        x += __shfl_xor(x, o);
-    return x;
+    x += dpp_i<0x128>(x);   // row_ror 8
+    x += dpp_i<0x124>(x);   // row_ror 4
+    x += dpp_i<0x122>(x);   // row_ror 2
+    x += dpp_i<0x121>(x);   // row_ror 1: every lane holds its row's total
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+           __builtin_amdgcn_readlane(x, 48);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o)
-            x += y;
-    }
-    return x;
+    // row_shr n: lane j reads lane j - n of its row, 0 for j < n
+    x += dpp_i<0x111>(x);
+    x += dpp_i<0x112>(x);
+    x += dpp_i<0x114>(x);
+    x += dpp_i<0x118>(x);   // scan within the row
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = lane / 16;
+    return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Context lengths of the first kLensRegs * 64 sequences, held in registers
@@ -505,10 +518,10 @@ __device__ __forceinline__ void locate(const DecodeParams &p, const Lens &lens, 
         if (mask) {
             const int first = __builtin_ctzll(mask);
             b_out = c + first;
-            start_out = (long long)(carry + __shfl(incl - nt, first)) * Hkv;
+            start_out = (long long)(carry + __builtin_amdgcn_readlane(incl - nt, first)) * Hkv;
             return;
         }
-        carry += __shfl(incl, 63);
+        carry += __builtin_amdgcn_readlane(incl, 63);
     }
     b_out = p.batch;
     start_out = 0;
