@@ -485,20 +485,29 @@ __device__ __forceinline__ int batch_tiles(const DecodeParams &p, const Lens &le
 // takes the same share.  Every share is non-empty when T >= 2 NW and
 // WA <= 2 WB (the kernels use H = NW otherwise).
 
+// a / b for wave-uniform non-negative operands: a 32-bit division when both
+// fit (always, in practice), else the 64-bit one.
+__device__ __forceinline__ long long div_nonneg(long long a, long long b)
+{
+    if (((unsigned long long)a | (unsigned long long)b) >> 32 == 0)
+        return (long long)((unsigned)a / (unsigned)b);
+    return a / b;
+}
+
 // First global tile of wave w's range.
 template <int WA, int WB>
 __device__ __forceinline__ long long range_start(long long w, long long T, long long NW, long long H)
 {
     static_assert(WB <= WA && WA <= 2 * WB, "share weights");
     const long long ws = w < H ? WA * w : WA * H + WB * (w - H);
-    return ws * T / (WA * H + WB * (NW - H));
+    return div_nonneg(ws * T, WA * H + WB * (NW - H));
 }
 
 // The wave that owns global tile t (largest w with range_start(w) <= t).
 template <int WA, int WB>
 __device__ __forceinline__ long long owner_of(long long t, long long T, long long NW, long long H)
 {
-    const long long x = ((t + 1) * (WA * H + WB * (NW - H)) - 1) / T;   // largest share start <= t
+    const long long x = div_nonneg((t + 1) * (WA * H + WB * (NW - H)) - 1, T);   // largest share start <= t
     return x < WA * H ? x / WA : min(NW - 1, H + (x - WA * H) / WB);
 }
 
@@ -785,8 +794,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void paged_decode_kernel(Decod
         cur.n = lens.of(p, cur.b);
         cur.nt = tiles_of(cur.n, p.max_context_len);
         const long long off = lo - start;
-        cur.g = (int)(off / cur.nt);
-        cur.k = (int)(off % cur.nt);
+        cur.g = (int)div_nonneg(off, cur.nt);
+        cur.k = (int)(off - (long long)cur.g * cur.nt);
         cur.make_uniform();
     }
     auto advance = [&](const Cursor &c) {
@@ -1393,8 +1402,8 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) __attribute__((amdgpu_waves_pe
         cur.n = lens.of(p, cur.b);
         cur.nt = tiles_of(cur.n, p.max_context_len);
         const long long off = lo - start;
-        cur.g = (int)(off / cur.nt);
-        cur.k = (int)(off % cur.nt);
+        cur.g = (int)div_nonneg(off, cur.nt);
+        cur.k = (int)(off - (long long)cur.g * cur.nt);
         cur.make_uniform();
     }
     auto advance = [&](const Cursor &x0) {
