@@ -11,4 +11,5 @@ from .pool import KVPool, kv_bytes  # noqa: F401
 from .sched import CONTINUOUS, STATIC, Scheduler  # noqa: F401
 from .serve import ServeLoop  # noqa: F401
 from .ops import (alloc_merge_counters, alloc_workspace, copy_pages, counter_bytes,  # noqa: F401
-                  decode_args, paged_attn_decode, paged_prefill, workspace_bytes, write_kv)
+                  decode_args, paged_attn_decode, paged_prefill, release_stream_buffers,
+                  workspace_bytes, write_kv)

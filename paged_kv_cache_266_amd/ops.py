@@ -128,8 +128,11 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     block_tables [B][max_blocks] int32; context_lens [B] int32 (device).
     ``max_context_len`` is a host-side bound on context_lens.  ``num_splits``
     is the number of waves sharing the batch's tiles (0 = library default).
-    ``workspace`` and ``merge_counters`` are allocated per call when not
-    given (see alloc_workspace, alloc_merge_counters).
+    When ``workspace`` or ``merge_counters`` is not given, a buffer kept per
+    (device, stream) is used, grown when a call needs more (see
+    _stream_buffers): calls on one stream run in order, so they can share
+    it, and the counters need no clearing because every call leaves them
+    zero.
     Returns ``out`` [B][Hq][D] in q's dtype.
     """
     import torch
@@ -139,17 +142,49 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     a = decode_args(q, k_pool, v_pool, block_tables, context_lens, scale,
                     max_context_len=max_context_len, out=out, k_scale=k_scale, v_scale=v_scale,
                     workspace=workspace, merge_counters=merge_counters, num_splits=num_splits)
-    if workspace is None:
-        workspace = alloc_workspace(a, q.device)
-        a.workspace = _ptr(workspace)
-        a.workspace_bytes = 0 if workspace is None else workspace.numel()
-    if merge_counters is None:
-        merge_counters = alloc_merge_counters(a, q.device)
-        a.merge_counters = _ptr(merge_counters)
-        a.merge_counter_bytes = 0 if merge_counters is None else 4 * merge_counters.numel()
-    check(lib().pkv_paged_attn_decode(ctypes.byref(a), _stream_handle(stream, q.device)),
-          "paged_attn_decode")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if workspace is None or merge_counters is None:
+        ws, ctr = _stream_buffers(a, q.device, stream)
+        if workspace is None:
+            a.workspace = _ptr(ws)
+            a.workspace_bytes = 0 if ws is None else ws.numel()
+        if merge_counters is None:
+            a.merge_counters = _ptr(ctr)
+            a.merge_counter_bytes = 0 if ctr is None else 4 * ctr.numel()
+    check(lib().pkv_paged_attn_decode(ctypes.byref(a), stream.cuda_stream), "paged_attn_decode")
     return out
+
+
+# (device index, stream handle) -> [workspace, merge counters]
+_STREAM_BUFFERS: dict = {}
+
+
+def _stream_buffers(args: DecodeArgs, device, stream):
+    """The workspace and merge counters kept for calls on ``stream``.
+
+    They are made on that stream, so when a larger call replaces them,
+    torch's allocator hands their memory out again only behind the work
+    already queued there.  A fresh counter array is zero; after that every
+    call leaves it zero.  One entry per stream a caller has used stays
+    until the process ends (or release_stream_buffers)."""
+    import torch
+
+    key = (torch.device(device).index, stream.cuda_stream)
+    entry = _STREAM_BUFFERS.setdefault(key, [None, None])
+    need_ws = workspace_bytes(args)
+    need_ctr = counter_bytes(args)
+    with torch.cuda.stream(stream):
+        if need_ws and (entry[0] is None or entry[0].numel() < need_ws):
+            entry[0] = torch.empty(need_ws, dtype=torch.uint8, device=device)
+        if need_ctr and (entry[1] is None or 4 * entry[1].numel() < need_ctr):
+            entry[1] = torch.zeros((need_ctr + 3) // 4, dtype=torch.int32, device=device)
+    return (entry[0] if need_ws else None), (entry[1] if need_ctr else None)
+
+
+def release_stream_buffers() -> None:
+    """Drop the buffers paged_attn_decode keeps per stream."""
+    _STREAM_BUFFERS.clear()
 
 
 def paged_prefill(q, k_pool, v_pool, block_tables, q_start, context_lens, scale: float, *,

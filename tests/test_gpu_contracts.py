@@ -327,3 +327,60 @@ def test_weighted_shares_more_waves_than_simds(qd, kvd, G):
     torch.cuda.synchronize()
     assert bool((out.view(torch.int16) == first.view(torch.int16)).all())
     assert int(ctr.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# The convenience call (no workspace, no counters given) keeps one pair of
+# buffers per stream: small and large batches in turn on two streams match
+# the explicit-buffer call bitwise, a repeat at a size already seen makes no
+# new device allocation, and the kept counters are zero afterwards.
+
+def test_convenience_call_keeps_buffers_per_stream():
+    import ctypes
+
+    import torch
+
+    import paged_kv_cache_266_amd as pkv
+    from paged_kv_cache_266_amd import ops
+    from paged_kv_cache_266_amd._lib import check, lib
+
+    pkv.release_stream_buffers()
+    small = make_case(small_config(8, 2, 128, "bf16", "bf16", 64, (300, 1000)), seed=31)
+    large = make_case(small_config(16, 4, 128, "bf16", "bf16", 16, (20000, 7, 9000, 4100)), seed=32)
+    cases = []
+    for case in (small, large):
+        dev = upload(case, "cuda")
+        out = torch.empty_like(dev.q)
+        a = pkv.decode_args(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                            max_context_len=case.cfg.max_context_len, out=out)
+        ws = pkv.alloc_workspace(a, "cuda")
+        ctr = pkv.alloc_merge_counters(a, "cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        a.merge_counters, a.merge_counter_bytes = ctr.data_ptr(), 4 * ctr.numel()
+        check(lib().pkv_paged_attn_decode(ctypes.byref(a), torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        compare(case, out, "explicit buffers")
+        cases.append((case, dev, out.clone(), torch.empty_like(dev.q)))
+
+    def call(i, stream=None):
+        case, dev, _, out = cases[i]
+        pkv.paged_attn_decode(dev.q, dev.k_pool, dev.v_pool, dev.block_tables, dev.context_lens, case.scale,
+                              max_context_len=case.cfg.max_context_len, out=out, stream=stream)
+
+    side = torch.cuda.Stream()
+    note("[convenience buffers] small, large, small, large on two streams")
+    for stream in (None, side):
+        for i in (0, 1, 0, 1):
+            call(i, stream)
+            torch.cuda.synchronize()
+            assert bool((cases[i][3].view(torch.int16) == cases[i][2].view(torch.int16)).all()), (i, stream)
+    assert len(ops._STREAM_BUFFERS) == 2
+    before = torch.cuda.memory_allocated()
+    for i in (1, 0, 1):
+        call(i)
+        call(i, side)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    for ws, ctr in ops._STREAM_BUFFERS.values():
+        assert ctr is not None and int(ctr.abs().sum()) == 0
+    pkv.release_stream_buffers()

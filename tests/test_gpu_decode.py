@@ -211,9 +211,11 @@ def test_gqa_equals_mha_with_repeated_kv():
     mha.cfg = get_config("tiny", **fields)
     mha.k_pages = np.repeat(case.k_pages, 4, axis=1)
     mha.v_pages = np.repeat(case.v_pages, 4, axis=1)
-    a = to_f64(gpu_decode(case))
-    b = to_f64(gpu_decode(mha))
-    assert np.abs(a - b).max() <= 1.6e-2
+    ga, gb = gpu_decode(case), gpu_decode(mha)
+    compare(case, ga, "G=4")
+    compare(mha, gb, "repeated KV, G=1")
+    assert np.allclose(oracle.paged_decode(case), oracle.paged_decode(mha), rtol=0, atol=1e-12)
+    assert np.abs(to_f64(ga) - to_f64(gb)).max() <= 1.6e-2
 
 
 def _two_launch(case, dev, num_splits=0):
