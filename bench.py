@@ -30,14 +30,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 COPY_CALIBRATION_MIB = 1024   # size of the plain copy the counters are calibrated on
-WARMUP_SECONDS = 0.25         # minimum untimed warm-up after the W warm-up steps
+WARMUP_SECONDS = 1.0          # minimum untimed warm-up after the W warm-up steps
 DEFAULT_CONFIG = "llama3_8b_gqa"
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="one decode workload (default: every decode workload, headline first, in one line)")
