@@ -192,6 +192,29 @@ def test_random_sweep_against_oracle():
         compare(case, gpu_decode(case, num_splits=splits), f"sweep {i}")
 
 
+# Larger batches (up to 47 sequences of up to 6000 tokens, up to 8 KV heads)
+# with wave counts above the number of SIMDs, where the waves dispatched
+# second on a SIMD take smaller shares, mixed with the small cases' shapes.
+
+def test_random_sweep_large_batches_against_oracle():
+    rng = np.random.default_rng(2027)
+    for i in range(24):
+        D = int(rng.choice([64, 128]))
+        PS = int(rng.choice([16, 64]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        qd, kvd = [("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"),
+                   ("f16", "fp8"), ("bf16", "fp8")][int(rng.integers(6))]
+        Hkv = int(rng.integers(1, 9))
+        B = int(rng.integers(8, 48))
+        pool = [0, 1, PS - 1, PS, PS + 1, 63, 64, 65, 127, 128, 129]
+        lens = tuple(int(rng.choice(pool)) if rng.random() < 0.3 else int(rng.integers(1, 6000)) for _ in range(B))
+        splits = int(rng.choice([0, int(rng.integers(4, 300)), int(rng.integers(1025, 3000))]))
+        note(f"[large sweep {i}] D={D} PS={PS} G={G} q={qd} kv={kvd} Hkv={Hkv} B={B} splits={splits}")
+        cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, lens)
+        case = make_case(cfg, seed=3000 + i, poison=bool(i % 3 == 0))
+        compare(case, gpu_decode(case, num_splits=splits), f"large sweep {i}")
+
+
 # ---------------------------------------------------------------------------
 # 200 back-to-back one-launch calls on one workspace and one counter array,
 # with many segments shared by several waves (the in-kernel merge on every

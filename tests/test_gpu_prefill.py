@@ -158,3 +158,27 @@ def test_prefill_large_chunks_sampled_rows(G, qd, kvd):
     ref_first = oracle.paged_prefill(early, first, qs8)
     got_first = np.concatenate([got[qs[b]:qs[b] + 8] for b in range(len(lens))])
     check(case, got_first, ref_first, "first 8 rows")
+
+
+def test_prefill_random_sweep_against_oracle():
+    """A seeded random sweep: head_dim, page size, group, dtype pair, KV
+    heads, ragged context lengths (page and tile boundaries among them) and
+    chunks (whole sequences, single tokens, parts), every row compared with
+    the oracle; stops at the first mismatch, naming the case."""
+    rng = np.random.default_rng(2028)
+    for i in range(40):
+        D = int(rng.choice([64, 128]))
+        PS = int(rng.choice([16, 64]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        qd = ["f16", "bf16"][int(rng.integers(2))]
+        kvd = [qd, "i8", "fp8"][int(rng.integers(3))]
+        Hkv = int(rng.integers(1, 4))
+        B = int(rng.integers(1, 7))
+        lens = [int(rng.choice([1, 2, PS - 1, PS, PS + 1, 64, 65, 129])) if rng.random() < 0.3
+                else int(rng.integers(1, 1200)) for _ in range(B)]
+        chunks = [n if rng.random() < 0.2 else int(rng.integers(1, min(n, 300) + 1)) for n in lens]
+        note(f"[prefill sweep {i}] D={D} PS={PS} G={G} q={qd} kv={kvd} Hkv={Hkv} lens={lens} chunks={chunks}")
+        cfg = small_config(G * Hkv, Hkv, D, qd, kvd, PS, tuple(lens))
+        case = make_case(cfg, seed=4000 + i)
+        qb, qs = queries(cfg, chunks, seed=i)
+        check(case, gpu_prefill(case, qb, qs), oracle.paged_prefill(case, qb, qs), f"prefill sweep {i}")
