@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import compare, gpu_decode, note, small_config, to_f64
+from gpu_helpers import TOL, compare, gpu_decode, note, small_config, to_f64
 from synth import CONFIGS, make_case
 from synth.configs import ORDER
 from synth.device import upload
@@ -241,21 +241,23 @@ def _two_launch(case, dev, num_splits=0):
     return out
 
 
-@pytest.mark.parametrize("lens,splits", [
-    ((4096, 3000, 777, 64, 0, 1), 0),        # ragged GQA batch, default grid
-    ((65536,), 1000),                        # one segment shared by 1000 waves: 4 merge levels
-    ((20000, 9, 20000), 300),
+@pytest.mark.parametrize("lens,splits,kvd", [
+    ((4096, 3000, 777, 64, 0, 1), 0, "bf16"),        # ragged GQA batch, default grid
+    ((65536,), 1000, "bf16"),                        # one segment shared by 1000 waves: 4 merge levels
+    ((20000, 9, 20000), 300, "bf16"),
+    ((20000, 9, 20000), 2000, "bf16"),               # more waves than SIMDs: weighted shares
+    ((20000, 9, 20000), 1500, "fp8"),                # the same on the matrix-core kernel
 ])
-def test_one_launch_and_two_launch_forms_agree(lens, splits):
-    cfg = small_config(32, 8, 128, "bf16", "bf16", 64, lens)
-    note(f"[fused vs two-launch] lens {lens} splits {splits}")
+def test_one_launch_and_two_launch_forms_agree(lens, splits, kvd):
+    cfg = small_config(32, 8, 128, "bf16", kvd, 64, lens)
+    note(f"[fused vs two-launch] lens {lens} splits {splits} kv {kvd}")
     case = make_case(cfg, seed=31)
     dev = upload(case, "cuda")
     one = gpu_decode(case, num_splits=splits, dev=dev)
     two = _two_launch(case, dev, num_splits=splits)
     compare(case, one, "one launch")
     compare(case, two, "two launches")
-    assert np.abs(to_f64(one) - to_f64(two)).max() <= 1.6e-2
+    assert np.abs(to_f64(one) - to_f64(two)).max() <= TOL[kvd]
 
 
 def test_buffers_reused_across_shapes_and_counters_return_to_zero():
