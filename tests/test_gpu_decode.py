@@ -299,3 +299,15 @@ def torch_equal_bits(a, b):
     import torch
 
     return bool(torch.equal(a.view(torch.int16), b.view(torch.int16)))
+
+
+@pytest.mark.parametrize("n,PS,kvd", [(1048576, 64, "bf16"), (393217, 16, "i8"), (524288, 64, "fp8")])
+def test_contexts_far_beyond_128k(n, PS, kvd):
+    """One sequence of up to a million tokens (contexts beyond 128k, GQA 32/8)
+    beside short ones, default wave count: every output against the oracle
+    (token, tile and block-table indices far past 2^16, pools over 2 GiB)."""
+    lens = (n, 3, 1000)
+    cfg = small_config(32, 8, 128, "bf16", kvd, PS, lens, num_pages=sum(-(-x // PS) for x in lens) + 40)
+    note(f"[long context] n={n} PS={PS} kv={kvd}")
+    case = make_case(cfg, seed=777)
+    compare(case, gpu_decode(case), f"{n} tokens")
