@@ -182,3 +182,26 @@ def test_prefill_random_sweep_against_oracle():
         case = make_case(cfg, seed=4000 + i)
         qb, qs = queries(cfg, chunks, seed=i)
         check(case, gpu_prefill(case, qb, qs), oracle.paged_prefill(case, qb, qs), f"prefill sweep {i}")
+
+
+@pytest.mark.parametrize("n,PS,kvd,G", [(262144, 64, "bf16", 4), (131077, 16, "i8", 1), (262144, 64, "fp8", 4)])
+def test_prefill_chunk_after_a_very_long_context(n, PS, kvd, G):
+    """A 512-token chunk at the end of a context of 131k or 262k tokens (and
+    one short sequence): the first and last 8 rows of each chunk against the
+    oracle, computed as 8-row chunks at the same positions."""
+    chunk = 512
+    lens = (n, 700)
+    Hkv = 8 if G == 4 else 16
+    cfg = small_config(G * Hkv, Hkv, 128, "bf16", kvd, PS, lens, num_pages=sum(-(-x // PS) for x in lens) + 40)
+    note(f"[prefill long context] n={n} PS={PS} kv={kvd} G={G}")
+    case = make_case(cfg, seed=21)
+    qb, qs = queries(cfg, (chunk, chunk), seed=22)
+    got = gpu_prefill(case, qb, qs)
+    qs8 = np.arange(0, 8 * len(lens) + 1, 8, dtype=np.int32)
+    last = np.concatenate([qb[qs[b + 1] - 8:qs[b + 1]] for b in range(len(lens))])
+    check(case, np.concatenate([got[qs[b + 1] - 8:qs[b + 1]] for b in range(len(lens))]),
+          oracle.paged_prefill(case, last, qs8), "last 8 rows")
+    first = np.concatenate([qb[qs[b]:qs[b] + 8] for b in range(len(lens))])
+    early = dataclasses.replace(case, context_lens=(case.context_lens - (chunk - 8)).astype(np.int32))
+    check(case, np.concatenate([got[qs[b]:qs[b] + 8] for b in range(len(lens))]),
+          oracle.paged_prefill(early, first, qs8), "first 8 rows")
