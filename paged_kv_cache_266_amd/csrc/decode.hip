@@ -1952,6 +1952,21 @@ __device__ __forceinline__ void quantise8(u32x4 w, u32 &lo, u32 &hi, float &s)
     }
     amax = group_max<L>(amax);
     s = fmaxf(amax, 1e-5f) / kQ;
+    // x / s, correctly rounded, with one division per row instead of one per
+    // value: y = RN(1 / s), then two of Markstein's corrections of x y (each
+    // q' = RN(q + (x - s q) y), the remainder exact through an fma).  x y is
+    // within two ulps of x / s, the first step brings it within one, and the
+    // second gives the correctly rounded quotient (P. Markstein, "Computation
+    // of elementary functions on the IBM RISC System/6000 processor", IBM J.
+    // Res. Dev. 34(1), 1990).  Quotients small enough for underflow to matter
+    // map to code 0 either way.  The quotient takes x's sign (s > 0): a -0
+    // stays -0, whose code differs from +0's.
+    const float y = 1.0f / s;
+    auto quot = [&](float v) {
+        float q = v * y;
+        q = fmaf(fmaf(-s, q, v), y, q);
+        return copysignf(fmaf(fmaf(-s, q, v), y, q), v);
+    };
     u32 word[2];
     if constexpr (KVT == I8) {
 #pragma unroll
@@ -1959,7 +1974,7 @@ __device__ __forceinline__ void quantise8(u32x4 w, u32 &lo, u32 &hi, float &s)
             u32 v = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float r = fminf(fmaxf(rintf(x[4 * h + e] / s), -127.0f), 127.0f);
+                const float r = fminf(fmaxf(rintf(quot(x[4 * h + e])), -127.0f), 127.0f);
                 v |= ((u32)(int)r & 0xFFu) << (8 * e);
             }
             word[h] = v;
@@ -1967,8 +1982,8 @@ __device__ __forceinline__ void quantise8(u32x4 w, u32 &lo, u32 &hi, float &s)
     } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h] / s, x[4 * h + 1] / s, 0, false);
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2] / s, x[4 * h + 3] / s, v, true);
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(quot(x[4 * h]), quot(x[4 * h + 1]), 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(quot(x[4 * h + 2]), quot(x[4 * h + 3]), v, true);
             word[h] = (u32)v;
         }
     }
