@@ -405,10 +405,11 @@ def bench_serve(args) -> None:
     (pkv_serve_step): the scheduler step (retire, admit, one token per
     running sequence), the staging of its slots, context lengths and block
     tables, the admitted prompts' and the new tokens' K/V appends, and the
-    decode of the mixed batch.  Requests: a backlog of 4 x batch requests
-    whose prompt lengths follow the workload's length law and which generate
-    32..256 tokens each (uniform), all arrived at step 0, at most `batch`
-    running.  K steps are timed after W warm-up steps: once as issued (the
+    decode of the mixed batch.  Requests: a backlog whose prompt lengths
+    follow the workload's length law and which generate 32..256 tokens each
+    (uniform, 144 on average), all arrived at step 0, at most `batch`
+    running; batch x (steps / 144 + 4) requests, so that the batch stays full
+    through the warm-up and both timed passes.  K steps are timed after W warm-up steps: once as issued (the
     host runs ahead of the GPU), once with HIP events around each step's
     device work, which give the GPU's busy time per step and the gaps between
     steps."""
@@ -428,8 +429,9 @@ def bench_serve(args) -> None:
     B, Hq, Hkv, D, PS = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
     byte = cfg.kv_dtype in ("i8", "fp8")
     src_t = cfg.q_dtype if byte else cfg.kv_dtype
-    n_req = 4 * B
-    prompts = np.concatenate([draw_context_lens(cfg, rng) for _ in range(4)])[:n_req]
+    rounds = -(-(args.warmup + 2 * args.steps) // 144) + 4
+    n_req = rounds * B
+    prompts = np.concatenate([draw_context_lens(cfg, rng) for _ in range(rounds)])[:n_req]
     new_tok = rng.integers(32, 257, size=n_req)
     cap = int(prompts.max() + new_tok.max())
     max_blocks = -(-cap // PS)
@@ -463,28 +465,37 @@ def bench_serve(args) -> None:
         loop.step()
     torch.cuda.synchronize()
 
-    # pass 1: as issued
-    tokens = 0
-    t0 = time.perf_counter()
-    host = wait = 0.0
-    for _ in range(args.steps):
-        h0 = time.perf_counter()
-        r = loop.step()
-        host += time.perf_counter() - h0
-        wait += r.slot_wait_us * 1e-6
-        tokens += r.sched.n_running
-    t_issue = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    # pass 2: events around each step's device work
-    evs = []
-    for _ in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        r = loop.step()
-        ev[1].record(stream)
-        evs.append(ev)
-    torch.cuda.synchronize()
+    # Python's collector stays off while the steps are issued (a collection
+    # would show as a gap between steps that the loop itself does not cause);
+    # the event pairs of pass 2 are made beforehand for the same reason
+    import gc
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    gc_on = gc.isenabled()
+    gc.disable()
+    try:
+        # pass 1: as issued
+        tokens = 0
+        t0 = time.perf_counter()
+        host = wait = 0.0
+        for _ in range(args.steps):
+            h0 = time.perf_counter()
+            r = loop.step()
+            host += time.perf_counter() - h0
+            wait += r.slot_wait_us * 1e-6
+            tokens += r.sched.n_running
+        t_issue = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        # pass 2: events around each step's device work
+        for ev in evs:
+            ev[0].record(stream)
+            loop.step()
+            ev[1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
     busy = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     gaps = [a_[1].elapsed_time(b_[0]) * 1e3 for a_, b_ in zip(evs, evs[1:])]
     st_ = sch.stats()
